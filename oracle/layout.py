@@ -24,8 +24,9 @@ Readings where the pages are silent (each one is also listed in the design notes
 * A token may name the same expert twice; each occurrence gets its own slot.
 * With dedup on, the send buffer is bucket-major and, inside a bucket, ordered by
   ascending token.  With dedup off the send rows are the slots.
-* An expert id outside [0, G) makes ``status`` = first bad flat index + 1 and leaves
-  the other outputs unspecified.
+* An expert id outside [0, G) makes ``status`` = first bad flat index + 1; a map
+  entry outside [0, B) makes it -(first bad expert + 1), checked first.  The pages
+  define no error behaviour; either way the other outputs are unspecified.
 
 Two formulations are given: ``dispatch_layout`` (array form, the one tests compare
 the GPU with) and ``dispatch_layout_loops`` (per-entry counting loops, for small
@@ -56,7 +57,11 @@ class Layout:
         return int(self.bucket_offset[-1])
 
 
-def _first_bad(flat: np.ndarray, G: int) -> int:
+def _first_bad(flat: np.ndarray, ebkt: np.ndarray, B: int) -> int:
+    bad_map = np.flatnonzero((ebkt < 0) | (ebkt >= B))
+    if bad_map.size:
+        return -(int(bad_map[0]) + 1)
+    G = ebkt.shape[0]
     bad = np.flatnonzero((flat < 0) | (flat >= G))
     return int(bad[0]) + 1 if bad.size else 0
 
@@ -69,7 +74,7 @@ def dispatch_layout(topk_idx: np.ndarray, expert_bucket: np.ndarray, B: int,
     ebkt = np.asarray(expert_bucket, dtype=np.int64)
     G = ebkt.shape[0]
     flat = idx.reshape(-1)
-    status = _first_bad(flat, G)
+    status = _first_bad(flat, ebkt, B)
     if status:
         return Layout(status=status)
 
@@ -117,6 +122,9 @@ def dispatch_layout_loops(topk_idx, expert_bucket, B: int, dedup: bool) -> Layou
     idx = [[int(e) for e in row] for row in np.asarray(topk_idx)]
     ebkt = [int(b) for b in np.asarray(expert_bucket)]
     M, k, G = len(idx), (len(idx[0]) if idx else 0), len(ebkt)
+    for e in range(G):
+        if not 0 <= ebkt[e] < B:
+            return Layout(status=-(e + 1))
     for t in range(M):
         for j in range(k):
             if not 0 <= idx[t][j] < G:

@@ -104,6 +104,10 @@ def test_invalid_expert_status():
         assert f(idx, ebkt, 1, False).status == 4      # flat index 3 is the first bad
     idx[1, 1] = 3
     assert dispatch_layout(idx, ebkt, 1, True).status == 5
+    # a bucket outside [0, B) is reported first, as -(expert + 1)
+    ebkt[2] = 1
+    for f in (dispatch_layout, dispatch_layout_loops):
+        assert f(idx, ebkt, 1, False).status == -3
 
 
 def check_invariants(w, lay, dedup):
