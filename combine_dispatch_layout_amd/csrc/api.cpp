@@ -1,0 +1,100 @@
+// C ABI of libmoedl: argument validation, workspace carving and kernel launches on
+// the caller's stream.  Every check here runs on the host before any HIP call, so a
+// rejected call touches neither the device nor the stream.
+#include <stdint.h>
+
+#include "moe_internal.h"
+
+namespace {
+
+constexpr int32_t kAbiVersion = 1;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+moe_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
+
+moe_status check_layout_sizes(int64_t M, int32_t k, int32_t G, int32_t B) {
+  if (M < 0 || k < 1 || G < 1 || B < 1 || k > G) return MOE_ERR_INVALID_ARGUMENT;
+  if (G > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK || B > MOE_MAX_BUCKETS) return MOE_ERR_UNSUPPORTED;
+  if (M * (int64_t)k >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return kAbiVersion; }
+
+const char* moe_status_string(moe_status status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported size or format";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+size_t moe_dispatch_layout_workspace_bytes(int64_t M, int32_t k, int32_t G, int32_t B) {
+  if (check_layout_sizes(M, k, G, B) != MOE_OK) return 0;
+  return moedl::layout_workspace_bytes(M, G, B);
+}
+
+moe_status moe_dispatch_layout(const int32_t* topk_idx, int64_t M, int32_t k,
+                               const int32_t* expert_bucket, int32_t G, int32_t B,
+                               int32_t dedup, int32_t* expert_count, int32_t* expert_offset,
+                               int32_t* bucket_count, int32_t* bucket_offset, int32_t* slot,
+                               int32_t* send_row, int32_t* send_token, int32_t* status,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const moe_status s = check_layout_sizes(M, k, G, B);
+  if (s != MOE_OK) return s;
+  if (!expert_bucket || !expert_count || !expert_offset || !bucket_count || !bucket_offset ||
+      !status || !workspace)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (M > 0 && (!topk_idx || !slot || !send_row || !send_token)) return MOE_ERR_INVALID_ARGUMENT;
+  if (dedup != 0 && dedup != 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(workspace)) return MOE_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < moedl::layout_workspace_bytes(M, G, B)) return MOE_ERR_WORKSPACE;
+  const moedl::LayoutWorkspace ws = moedl::carve_layout_workspace(workspace, M, G, B);
+  return from_hip(moedl::launch_layout(topk_idx, M, k, expert_bucket, G, B, dedup, expert_count,
+                                       expert_offset, bucket_count, bucket_offset, slot,
+                                       send_row, send_token, status, ws, stream));
+}
+
+moe_status moe_dispatch(const void* x, moe_dtype dtype, int64_t M, int32_t N,
+                        const float* x_scale, const int32_t* send_row, int32_t k, void* out,
+                        float* out_scale, int64_t out_rows, hipStream_t stream) {
+  if (M < 0 || N < 1 || k < 1 || out_rows < 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (dtype != MOE_BF16 && dtype != MOE_FP8_E4M3) return MOE_ERR_INVALID_ARGUMENT;
+  if (k > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
+  if ((x_scale == nullptr) != (out_scale == nullptr)) return MOE_ERR_INVALID_ARGUMENT;
+  if (x_scale && dtype != MOE_FP8_E4M3) return MOE_ERR_INVALID_ARGUMENT;
+  const int64_t row_bytes = (int64_t)N * (dtype == MOE_BF16 ? 2 : 1);
+  if (row_bytes % 16 != 0) return MOE_ERR_UNSUPPORTED;
+  if (x_scale && N % MOE_SCALE_BLOCK != 0) return MOE_ERR_UNSUPPORTED;
+  if (M > 0 && (!x || !send_row)) return MOE_ERR_INVALID_ARGUMENT;
+  if (out_rows > 0 && !out) return MOE_ERR_INVALID_ARGUMENT;
+  if ((x && !aligned16(x)) || (out && !aligned16(out))) return MOE_ERR_INVALID_ARGUMENT;
+  if (x_scale && (((uintptr_t)x_scale & 3u) || ((uintptr_t)out_scale & 3u)))
+    return MOE_ERR_INVALID_ARGUMENT;
+  const int32_t scale_cols = x_scale ? N / MOE_SCALE_BLOCK : 0;
+  return from_hip(moedl::launch_dispatch(x, M, row_bytes, x_scale, scale_cols, send_row, k, out,
+                                         out_scale, out_rows, stream));
+}
+
+moe_status moe_combine(const uint16_t* expert_out, int64_t expert_rows, const float* weights,
+                       const int32_t* slot, int64_t M, int32_t k, int32_t N, uint16_t* y,
+                       hipStream_t stream) {
+  if (M < 0 || N < 1 || k < 1 || expert_rows < 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (k > MOE_MAX_TOPK || N % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if (M > 0 && (!weights || !slot || !y)) return MOE_ERR_INVALID_ARGUMENT;
+  if (expert_rows > 0 && !expert_out) return MOE_ERR_INVALID_ARGUMENT;
+  if ((expert_out && !aligned16(expert_out)) || (y && !aligned16(y)))
+    return MOE_ERR_INVALID_ARGUMENT;
+  return from_hip(
+      moedl::launch_combine(expert_out, expert_rows, weights, slot, M, k, N, y, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,67 @@
+// Internal declarations shared by the libmoedl translation units: kernel
+// launchers (one per .hip file) and the small wave-level helpers every kernel uses.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe_dispatch.h"
+
+namespace moedl {
+
+// ---------------------------------------------------------------- layout tiling
+// One layout tile = 256 tokens = one 256-thread workgroup (4 wave64s, 64 tokens
+// each).  Per-tile partial counts live in the caller's workspace.
+constexpr int kTileTokens = 256;
+constexpr int kTileThreads = 256;
+constexpr int kTileWaves = kTileThreads / 64;
+constexpr int kScanThreads = 1024;
+constexpr int kNoError = 0x7FFFFFFF;
+
+struct LayoutWorkspace {
+  int32_t* tile_hist;   // [T][G]: per-tile expert counts, then their column prefix
+  int32_t* tile_bhist;  // [T][B]: per-tile distinct (token, bucket) counts, then prefix
+  int32_t* tile_err;    // [T]:    first bad flat index in the tile, or kNoError
+};
+
+inline int64_t layout_tiles(int64_t M) { return (M + kTileTokens - 1) / kTileTokens; }
+
+size_t layout_workspace_bytes(int64_t M, int32_t G, int32_t B);
+LayoutWorkspace carve_layout_workspace(void* base, int64_t M, int32_t G, int32_t B);
+
+hipError_t launch_layout(const int32_t* topk_idx, int64_t M, int32_t k,
+                         const int32_t* expert_bucket, int32_t G, int32_t B, int32_t dedup,
+                         int32_t* expert_count, int32_t* expert_offset,
+                         int32_t* bucket_count, int32_t* bucket_offset, int32_t* slot,
+                         int32_t* send_row, int32_t* send_token, int32_t* status,
+                         const LayoutWorkspace& ws, hipStream_t stream);
+
+hipError_t launch_dispatch(const void* x, int64_t M, int64_t row_bytes,
+                           const float* x_scale, int32_t scale_cols,
+                           const int32_t* send_row, int32_t k, void* out,
+                           float* out_scale, int64_t out_rows, hipStream_t stream);
+
+hipError_t launch_combine(const uint16_t* expert_out, int64_t expert_rows,
+                          const float* weights, const int32_t* slot, int64_t M,
+                          int32_t k, int32_t N, uint16_t* y, hipStream_t stream);
+
+// ---------------------------------------------------------------- device helpers
+#if defined(__HIP_DEVICE_COMPILE__) || defined(__HIPCC__)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint64_t wave_ballot(bool p) {
+  return __builtin_amdgcn_ballot_w64(p);
+}
+// Number of set bits of `mask` in lanes below the calling lane.
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+__device__ __forceinline__ int wave_index() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+#endif
+
+}  // namespace moedl

@@ -1,0 +1,192 @@
+"""Thin Python binding over libmoedl (include/moe_dispatch.h).
+
+Argument marshalling only: every step of the path runs in the library's HIP kernels.
+torch is used for device memory and streams -- tensors' data pointers and the
+current HIP stream are passed straight through.  Output tensors are allocated here
+when the caller does not pass them.  There is no fallback: if the shared library is
+missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoedl.so")
+
+MOE_OK = 0
+MOE_BF16 = 0
+MOE_FP8_E4M3 = 1
+MAX_EXPERTS = 1024
+MAX_TOPK = 16
+MAX_BUCKETS = 64
+SCALE_BLOCK = 128
+
+_lib: Optional[ctypes.CDLL] = None
+
+_i32p = ctypes.c_void_p
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+
+# name -> (restype, argtypes), mirroring include/moe_dispatch.h
+SIGNATURES = {
+    "moe_abi_version": (ctypes.c_int32, []),
+    "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "moe_dispatch_layout_workspace_bytes": (ctypes.c_size_t, [_i64, _i32, _i32, _i32]),
+    "moe_dispatch_layout": (ctypes.c_int, [
+        _i32p, _i64, _i32, _i32p, _i32, _i32, _i32, _i32p, _i32p, _i32p, _i32p, _i32p,
+        _i32p, _i32p, _i32p, _vp, ctypes.c_size_t, _vp]),
+    "moe_dispatch": (ctypes.c_int, [
+        _vp, ctypes.c_int, _i64, _i32, _vp, _i32p, _i32, _vp, _vp, _i64, _vp]),
+    "moe_combine": (ctypes.c_int, [_vp, _i64, _vp, _i32p, _i64, _i32, _i32, _vp, _vp]),
+}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, call: str, status: int):
+        self.status = status
+        msg = lib().moe_status_string(status).decode() if _lib is not None else str(status)
+        super().__init__(f"{call} failed: status {status} ({msg})")
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libmoedl.so (built by combine_dispatch_layout_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: run `python -m combine_dispatch_layout_amd.build`")
+        lib_ = ctypes.CDLL(path)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib_, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib_
+    return _lib
+
+
+def lib() -> ctypes.CDLL:
+    return load()
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if t.device.type != "cuda":
+        raise ValueError("tensors passed to libmoedl must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libmoedl must be contiguous")
+    return t.data_ptr() if t.numel() > 0 else None
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(call: str, status: int) -> None:
+    if status != MOE_OK:
+        raise MoeError(call, status)
+
+
+def workspace_bytes(M: int, k: int, G: int, B: int) -> int:
+    return int(lib().moe_dispatch_layout_workspace_bytes(M, k, G, B))
+
+
+@dataclass
+class Layout:
+    expert_count: torch.Tensor   # int32 [G]
+    expert_offset: torch.Tensor  # int32 [G]
+    bucket_count: torch.Tensor   # int32 [B]
+    bucket_offset: torch.Tensor  # int32 [B+1]
+    slot: torch.Tensor           # int32 [M, k]
+    send_row: torch.Tensor       # int32 [M, k]
+    send_token: torch.Tensor     # int32 [capacity]
+    status: torch.Tensor         # int32 [1]
+    workspace: torch.Tensor      # uint8 scratch
+    dedup: bool
+
+    @property
+    def capacity(self) -> int:
+        return self.send_token.numel()
+
+
+def send_capacity(M: int, k: int, B: int, dedup: bool) -> int:
+    """Rows the send buffer needs, known on the host: M*k, or M*min(k, B) with dedup."""
+    return M * (min(k, B) if dedup else k)
+
+
+def alloc_layout(M: int, k: int, G: int, B: int, dedup: bool, device="cuda") -> Layout:
+    i32 = dict(dtype=torch.int32, device=device)
+    return Layout(
+        expert_count=torch.empty(G, **i32), expert_offset=torch.empty(G, **i32),
+        bucket_count=torch.empty(B, **i32), bucket_offset=torch.empty(B + 1, **i32),
+        slot=torch.empty((M, k), **i32), send_row=torch.empty((M, k), **i32),
+        send_token=torch.empty(send_capacity(M, k, B, dedup), **i32),
+        status=torch.empty(1, **i32),
+        workspace=torch.empty(max(1, workspace_bytes(M, k, G, B)), dtype=torch.uint8,
+                              device=device),
+        dedup=dedup)
+
+
+def moe_dispatch_layout(topk_idx: torch.Tensor, expert_bucket: torch.Tensor, B: int,
+                        dedup: bool, out: Optional[Layout] = None, stream=None) -> Layout:
+    """topk_idx int32 [M, k], expert_bucket int32 [G] -> Layout (device tensors)."""
+    M, k = topk_idx.shape
+    G = expert_bucket.shape[0]
+    if topk_idx.dtype != torch.int32 or expert_bucket.dtype != torch.int32:
+        raise TypeError("topk_idx and expert_bucket must be int32")
+    lay = out if out is not None else alloc_layout(M, k, G, B, dedup, topk_idx.device)
+    st = lib().moe_dispatch_layout(
+        _ptr(topk_idx), M, k, _ptr(expert_bucket), G, B, int(dedup), _ptr(lay.expert_count),
+        _ptr(lay.expert_offset), _ptr(lay.bucket_count), _ptr(lay.bucket_offset),
+        _ptr(lay.slot), _ptr(lay.send_row), _ptr(lay.send_token), _ptr(lay.status),
+        _ptr(lay.workspace), lay.workspace.numel(), _stream(stream))
+    _check("moe_dispatch_layout", st)
+    return lay
+
+
+def _dtype_code(x: torch.Tensor) -> int:
+    if x.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        return MOE_BF16
+    if x.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return MOE_FP8_E4M3
+    raise TypeError(f"unsupported row dtype {x.dtype}")
+
+
+def moe_dispatch(x: torch.Tensor, send_row: torch.Tensor, out_rows: int,
+                 x_scale: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                 out_scale: Optional[torch.Tensor] = None, stream=None):
+    """x [M, N] (bf16 bits or fp8 codes), send_row int32 [M, k] -> (out [out_rows, N],
+    out_scale [out_rows, N/128] or None)."""
+    M, N = x.shape
+    k = send_row.shape[1] if send_row.dim() == 2 else 1
+    if out is None:
+        out = torch.empty((out_rows, N), dtype=x.dtype, device=x.device)
+    if x_scale is not None and out_scale is None:
+        out_scale = torch.empty((out_rows, x_scale.shape[1]), dtype=torch.float32,
+                                device=x.device)
+    st = lib().moe_dispatch(_ptr(x), _dtype_code(x), M, N, _ptr(x_scale), _ptr(send_row), k,
+                            _ptr(out), _ptr(out_scale), out_rows, _stream(stream))
+    _check("moe_dispatch", st)
+    return out, out_scale
+
+
+def moe_combine(expert_out: torch.Tensor, weights: torch.Tensor, slot: torch.Tensor,
+                y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """expert_out bf16 [rows, N], weights fp32 [M, k], slot int32 [M, k] -> y bf16 [M, N]."""
+    rows, N = expert_out.shape
+    M, k = slot.shape
+    if weights.dtype != torch.float32:
+        raise TypeError("weights must be float32")
+    if y is None:
+        y = torch.empty((M, N), dtype=expert_out.dtype, device=expert_out.device)
+    st = lib().moe_combine(_ptr(expert_out), rows, _ptr(weights), _ptr(slot), M, k, N, _ptr(y),
+                           _stream(stream))
+    _check("moe_combine", st)
+    return y

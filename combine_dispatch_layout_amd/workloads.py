@@ -300,8 +300,10 @@ def make_custom(M: int, N: int, G: int, k: int, B: int, dtype: str = "bf16",
     else:
         raise ValueError(bucket_map)
     w = softmax_weights(rng, M, k)
-    if dtype == "fp8":
+    if dtype == "fp8" and N % FP8_BLOCK == 0:
         x, xs = normal_fp8_rows(rng, M, N)
+    elif dtype == "fp8":                # no whole 128-blocks: raw codes, no scales
+        x, xs = rng.integers(0, 256, size=(M, N), dtype=np.uint8), None
     else:
         x, xs = normal_bf16_rows(rng, M, N), None
     return Workload(name=f"custom-M{M}-N{N}-G{G}-k{k}-B{B}-{routing}", cfg_id=0, M=M, N=N,

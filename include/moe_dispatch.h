@@ -1,0 +1,185 @@
+/*
+ * moe_dispatch.h -- C ABI of libmoedl: MoE token dispatch layout, dispatch and
+ * combine on one AMD Instinct MI355X (gfx950).
+ *
+ * The three calls are one GPU's share of expert-parallel all-to-all dispatch and
+ * combine, as the problem is stated in "All2all performance comparison between
+ * Triton-distributed and DeepEP" (sections "Test Code Snippet" and "Benchmark
+ * Configuration"): M tokens of hidden size N (HIDDEN), G experts in total
+ * (NUM_TOT_EXPERTS), top-k routing, experts grouped into destinations
+ * (EXPERTS_PER_RANK, WORLD_SIZE; here "buckets" with an arbitrary expert -> bucket
+ * map), an element size of 2 (bf16) or 1 (fp8) bytes with optional per-block
+ * scales (WITH_SCALE, SCALE_ELEMENT_SIZE), and per-destination splits with their
+ * cumulative sums.
+ *
+ * Conventions shared by every call:
+ *  - Every pointer argument is a DEVICE pointer (hipMalloc'd or torch memory),
+ *    except where a comment says otherwise.  The caller owns and allocates every
+ *    buffer, including the layout workspace; the library allocates nothing, keeps
+ *    no global state and has no handle.
+ *  - Calls are asynchronous on `stream` (0 = the legacy default stream) and never
+ *    synchronise the host.  Outputs are valid once the stream reaches them.
+ *  - Host-checkable argument errors are returned synchronously, before any
+ *    launch, as a moe_status; nothing is written in that case.
+ *  - Data-dependent errors (an expert id or bucket id out of range) are reported
+ *    in the device status word written by moe_dispatch_layout; the layout outputs
+ *    are then unspecified but every kernel stays in bounds.
+ *  - All row buffers are row-major with a row pitch equal to the row size; row
+ *    bases must be 16-byte aligned and row sizes a multiple of 16 bytes.
+ *  - Calls are reentrant across streams as long as their output buffers and
+ *    workspaces differ.
+ */
+#ifndef MOE_DISPATCH_H_
+#define MOE_DISPATCH_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative size, k > G, misaligned */
+  MOE_ERR_UNSUPPORTED = 2,      /* beyond the limits below */
+  MOE_ERR_WORKSPACE = 3,        /* workspace smaller than the query returns */
+  MOE_ERR_LAUNCH = 4            /* the HIP runtime refused a kernel launch */
+} moe_status;
+
+typedef enum moe_dtype {
+  MOE_BF16 = 0,     /* bfloat16, 2 bytes per element */
+  MOE_FP8_E4M3 = 1  /* OCP fp8 e4m3 ("fn": no infinities, max 448), 1 byte */
+} moe_dtype;
+
+#define MOE_MAX_EXPERTS 1024 /* G */
+#define MOE_MAX_TOPK 16      /* k */
+#define MOE_MAX_BUCKETS 64   /* B */
+#define MOE_SCALE_BLOCK 128  /* elements per fp32 scale */
+
+/* Version of this ABI (bumped on any signature change). */
+int32_t moe_abi_version(void);
+
+/* Static, NUL-terminated description of a status (host pointer). */
+const char* moe_status_string(moe_status status);
+
+/*
+ * Bytes of device workspace moe_dispatch_layout needs for these sizes (a pure
+ * host computation; 0 if the sizes are invalid).  The workspace holds per-tile
+ * partial counts; it needs no initialisation and may be reused by any later call
+ * on the same stream.
+ */
+size_t moe_dispatch_layout_workspace_bytes(int64_t M, int32_t k, int32_t G, int32_t B);
+
+/*
+ * moe_dispatch_layout -- counts, cumulative offsets, the stable slot map and the
+ * send-row map of one routing batch.
+ *
+ * Passages: the send buffer grouped by destination, its splits and cumulative sums
+ * ("All2all performance comparison ...", "Test Code Snippet"); per-expert row
+ * offsets that stay on the device for a grouped GEMM ("Add Triton grouped-GEMM for
+ * MoE experts on Ampere/Ada", "What this PR does"); a token sent to a destination
+ * only once however many of its experts live there ("Zyphra says routing-pattern
+ * expert placement ...", the 58% copy-reduction item).
+ *
+ * Inputs:
+ *   topk_idx      int32 [M*k], row-major [M][k]: expert id of token t's j-th choice,
+ *                 in [0, G).  A token may repeat an expert; each repeat is its own
+ *                 entry.
+ *   expert_bucket int32 [G]: destination bucket of each expert, in [0, B).
+ *   dedup         0: one send row per (t, j).  1: one send row per distinct
+ *                 (t, bucket).
+ * Outputs (all written by this call; M may be 0):
+ *   expert_count  int32 [G]: entries routed to each expert (sum = M*k).
+ *   expert_offset int32 [G]: first slot of each expert's run.  Runs are laid out
+ *                 in (bucket, expert id) order, so expert_offset/expert_count are
+ *                 the grouped-GEMM `offs` of the per-expert buffers.
+ *   bucket_count  int32 [B]: send rows of each bucket (the splits).
+ *   bucket_offset int32 [B+1]: exclusive cumulative sum of bucket_count;
+ *                 bucket_offset[B] = R, the number of send rows.
+ *   slot          int32 [M*k]: position of entry (t, j) in slot space: its expert's
+ *                 offset plus the number of earlier entries (ascending t, then j)
+ *                 routed to the same expert.  A bijection onto [0, M*k).
+ *   send_row      int32 [M*k]: send-buffer row of entry (t, j).  dedup=0: equals
+ *                 slot.  dedup=1: bucket_offset[b] + number of tokens t' < t that
+ *                 also send to b, where b = expert_bucket[topk_idx[t,j]].
+ *   send_token    int32 [capacity]: token of each send row, rows [0, R) written.
+ *                 Capacity M*k (dedup=0) or M*min(k, B) (dedup=1).
+ *   status        int32 [1]: 0 when all ids are valid; t*k + j + 1 for the first
+ *                 entry whose expert id is outside [0, G); -(e + 1) for the first
+ *                 expert e whose bucket is outside [0, B) (checked first).
+ *   workspace     device scratch of at least
+ *                 moe_dispatch_layout_workspace_bytes(M, k, G, B) bytes, 16-byte
+ *                 aligned; overwritten.
+ * Errors: MOE_ERR_INVALID_ARGUMENT (M < 0, k < 1, k > G, G < 1, B < 1, a null
+ * pointer for a non-empty array), MOE_ERR_UNSUPPORTED (G > 1024, k > 16, B > 64,
+ * M*k >= 2^31), MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH.
+ */
+moe_status moe_dispatch_layout(const int32_t* topk_idx, int64_t M, int32_t k,
+                               const int32_t* expert_bucket, int32_t G, int32_t B,
+                               int32_t dedup, int32_t* expert_count,
+                               int32_t* expert_offset, int32_t* bucket_count,
+                               int32_t* bucket_offset, int32_t* slot, int32_t* send_row,
+                               int32_t* send_token, int32_t* status, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_dispatch -- copy each token's row (and its scales) into its send rows.
+ *
+ * Passage: the gather of token rows into the destination-grouped send buffer, with
+ * scales travelling beside fp8 data ("All2all performance comparison ...", "Test
+ * Code Snippet" and the note under "Results").  Each x row is read once and written
+ * once to every distinct row among send_row[t, 0..k).
+ *
+ * Inputs:
+ *   x         [M, N] elements of `dtype`, row-major; 16-byte aligned.
+ *   x_scale   float [M, N/128] or NULL.  Only with MOE_FP8_E4M3, and then
+ *             N % 128 == 0.
+ *   send_row  int32 [M*k] from moe_dispatch_layout (any map into rows works).
+ * Outputs:
+ *   out       [out_rows, N] elements of `dtype`; rows named by send_row are written.
+ *   out_scale float [out_rows, N/128]; NULL exactly when x_scale is NULL.
+ *   out_rows  capacity of out in rows.  Entries of send_row outside [0, out_rows)
+ *             are skipped, so an erroneous layout can never write out of bounds.
+ * Errors: MOE_ERR_INVALID_ARGUMENT (null or misaligned pointers, M < 0, N < 1,
+ * k < 1, scales with bf16, out_scale/x_scale mismatch), MOE_ERR_UNSUPPORTED (row
+ * bytes not a multiple of 16, scales with N % 128 != 0, k > 16), MOE_ERR_LAUNCH.
+ */
+moe_status moe_dispatch(const void* x, moe_dtype dtype, int64_t M, int32_t N,
+                        const float* x_scale, const int32_t* send_row, int32_t k,
+                        void* out, float* out_scale, int64_t out_rows,
+                        hipStream_t stream);
+
+/*
+ * moe_combine -- routing-weighted top-k sum of expert outputs back in token order.
+ *
+ *   y[t, i] = bf16_rne( sum_{j=0..k-1} w[t, j] * expert_out[slot[t, j], i] )
+ *
+ * with an fp32 accumulator that starts at +0.0 and takes, for j ascending, one
+ * rounded fp32 product and one rounded fp32 add (no fused multiply-add), then one
+ * round-to-nearest-even to bf16.  This is the determinism rule of "Purlin:
+ * Separating Orchestration from the Datapath of Collectives", section 3.3 (SCORE):
+ * one owner per output element, accumulation in source order.  Results are
+ * bitwise reproducible.
+ *
+ * Inputs:
+ *   expert_out  bf16 [expert_rows, N], slot-indexed (expert-major); 16-byte
+ *               aligned.
+ *   weights     float [M*k], row-major [M][k]; never renormalised.
+ *   slot        int32 [M*k] from moe_dispatch_layout.  Entries outside
+ *               [0, expert_rows) contribute nothing.
+ * Output:
+ *   y           bf16 [M, N]; 16-byte aligned.
+ * Errors: MOE_ERR_INVALID_ARGUMENT (null or misaligned pointers, M < 0, N < 1,
+ * k < 1), MOE_ERR_UNSUPPORTED (N % 8 != 0, k > 16), MOE_ERR_LAUNCH.
+ */
+moe_status moe_combine(const uint16_t* expert_out, int64_t expert_rows,
+                       const float* weights, const int32_t* slot, int64_t M, int32_t k,
+                       int32_t N, uint16_t* y, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_DISPATCH_H_ */

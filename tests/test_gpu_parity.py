@@ -1,0 +1,239 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the same
+seeded inputs.
+
+Layout, counts, slot/send maps and dispatched rows must match bit for bit; combine
+must match the oracle's bf16 output bit for bit (the oracle fixes the fp32 op order,
+so the 2e-3 relative tolerance on bf16 outputs leaves no room for any other
+result; the relative error is also computed and checked against 2e-3).
+
+Sizes: every standard workload at a reduced token count that spans several
+256-token layout tiles with a ragged last tile (full comparison), and at its full
+size (full comparison of layout and dispatch, combine on sampled tokens) in the
+launch configuration the bench times.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from combine_dispatch_layout_amd import workloads as wl
+from gpu_util import (assert_bits_equal, assert_dispatch_equal, assert_layout_equal, dev,
+                      gpu_combine, gpu_dispatch, gpu_expert_outputs, gpu_layout, host,
+                      oracle_combine_tokens, oracle_pipeline, say)
+
+pytestmark = pytest.mark.gpu
+
+REL_TOL = 2e-3
+
+
+def max_rel_err(got_u16, want_u16):
+    g = oracle.bf16_to_f32(got_u16.view(np.uint16)).astype(np.float64)
+    r = oracle.bf16_to_f32(want_u16).astype(np.float64)
+    nz = r != 0
+    assert np.all(g[~nz] == 0)
+    return float(np.max(np.abs(g[nz] - r[nz]) / np.abs(r[nz]))) if nz.any() else 0.0
+
+
+REDUCED = [  # (cfg, M, map_kind)
+    (1, None, "pair"), (2, 1000, "pair"), (3, 1000, "pair"), (4, 1000, "pair"),
+    (4, 1000, "roundrobin"), (5, 300, "pair"),
+]
+
+
+@pytest.mark.parametrize("cfg,M,map_kind", REDUCED)
+@pytest.mark.parametrize("dedup", [False, True])
+def test_pipeline_reduced(gpu_lib, cfg, M, map_kind, dedup):
+    w = wl.make_workload(cfg, M=M, map_kind=map_kind)
+    ctx = f"{w.name} M={w.M} dedup={dedup}"
+    say(ctx)
+    ref, sent, sent_scale, eo_ref, y_ref = oracle_pipeline(w, dedup)
+    lay = gpu_layout(w, dedup)
+    assert_layout_equal(lay, ref, ctx)
+    out, out_scale = gpu_dispatch(w, lay)
+    assert_dispatch_equal(w, out, out_scale, ref, ctx=ctx)
+    eo = gpu_expert_outputs(w, lay, out, out_scale)
+    y = gpu_combine(w, lay, eo)
+    torch.cuda.synchronize()
+    got = host(y)
+    assert max_rel_err(got, y_ref) <= REL_TOL
+    assert_bits_equal(got, y_ref, ctx)
+
+
+@pytest.mark.parametrize("cfg,map_kind", [(1, "pair"), (2, "pair"), (3, "pair"), (4, "pair"),
+                                          (4, "roundrobin"), (5, "pair")])
+@pytest.mark.parametrize("dedup", [False, True])
+def test_layout_full_size(gpu_lib, cfg, map_kind, dedup):
+    w = wl.make_workload(cfg, map_kind=map_kind, with_rows=False)
+    say(f"layout {w.name} M={w.M} dedup={dedup}")
+    ref = oracle.dispatch_layout(w.topk_idx, w.expert_bucket, w.B, dedup)
+    assert_layout_equal(gpu_layout(w, dedup), ref, w.name)
+
+
+@pytest.fixture(scope="module")
+def cfg3():
+    return wl.make_workload(3)
+
+
+@pytest.mark.parametrize("dedup", [False, True])
+def test_bench_workload_full_size(gpu_lib, cfg3, dedup):
+    """Zipf(1.2) M=16384 N=7168 G=256 top-8: the bench's workload and launch
+    configuration (combine reads the dispatched rows in place when dedup is off)."""
+    w = cfg3
+    say(f"full {w.name} dedup={dedup}")
+    ref = oracle.dispatch_layout(w.topk_idx, w.expert_bucket, w.B, dedup)
+    lay = gpu_layout(w, dedup)
+    assert_layout_equal(lay, ref, w.name)
+    out, out_scale = gpu_dispatch(w, lay)
+    assert_dispatch_equal(w, out, out_scale, ref, ctx=w.name)
+    eo = gpu_expert_outputs(w, lay, out, out_scale)
+    y = gpu_combine(w, lay, eo)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(99)
+    tokens = np.sort(rng.choice(w.M, size=384, replace=False))
+    tokens[0], tokens[-1] = 0, w.M - 1
+    want = oracle_combine_tokens(w, ref, tokens)
+    got = host(y[dev(tokens).long()])
+    assert max_rel_err(got, want) <= REL_TOL
+    assert_bits_equal(got, want, w.name)
+    # identity experts: every output row is its input row (closed form)
+    x = torch.from_numpy(w.x.view(np.int16)).cuda()
+    x = torch.where(x == -32768, torch.zeros_like(x), x)       # -0 comes back as +0
+    assert bool((y == x).all().item())
+
+
+def test_fp8_workload_full_size(gpu_lib):
+    """M=65536, fp8 e4m3 rows + fp32 per-128 scales, > 2^31-byte buffers."""
+    w = wl.make_workload(5)
+    say(f"full {w.name}")
+    ref = oracle.dispatch_layout(w.topk_idx, w.expert_bucket, w.B, False)
+    lay = gpu_layout(w, False)
+    assert_layout_equal(lay, ref, w.name)
+    out, out_scale = gpu_dispatch(w, lay, sentinel=False)
+    assert_dispatch_equal(w, out, out_scale, ref, chunk=65536, ctx=w.name)
+    eo = gpu_expert_outputs(w, lay, out, out_scale)
+    del out
+    y = gpu_combine(w, lay, eo)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    tokens = np.sort(rng.choice(w.M, size=256, replace=False))
+    tokens[-1] = w.M - 1
+    want = oracle_combine_tokens(w, ref, tokens)
+    got = host(y[dev(tokens).long()])
+    assert_bits_equal(got, want, w.name)
+
+
+@pytest.mark.parametrize("cfg,map_kind", [(2, "pair"), (4, "pair"), (4, "roundrobin")])
+def test_full_size_full_compare(gpu_lib, cfg, map_kind):
+    w = wl.make_workload(cfg, map_kind=map_kind)
+    say(f"full {w.name}")
+    ref, sent, sent_scale, eo_ref, y_ref = oracle_pipeline(w, w.dedup)
+    lay = gpu_layout(w, w.dedup)
+    assert_layout_equal(lay, ref, w.name)
+    out, out_scale = gpu_dispatch(w, lay)
+    assert_dispatch_equal(w, out, out_scale, ref, ctx=w.name)
+    y = gpu_combine(w, lay, gpu_expert_outputs(w, lay, out, out_scale))
+    torch.cuda.synchronize()
+    got = host(y)
+    assert max_rel_err(got, y_ref) <= REL_TOL
+    assert_bits_equal(got, y_ref, w.name)
+
+
+EDGE = [  # (M, N, G, k, B, dtype, routing, bucket_map)
+    (1, 7168, 256, 8, 8, "bf16", "uniform", "contiguous"),
+    (2, 8, 4, 1, 1, "bf16", "uniform", "contiguous"),           # one 16-byte vector rows
+    (257, 64, 1, 1, 1, "bf16", "uniform", "contiguous"),         # G = 1
+    (300, 128, 16, 4, 4, "bf16", "one_expert", "contiguous"),    # all to one expert
+    (513, 136, 37, 5, 3, "bf16", "repeats", "random"),           # duplicates, odd shapes
+    (700, 1024, 1024, 16, 64, "bf16", "uniform", "random"),      # maximum G, k, B
+    (640, 512, 96, 6, 7, "bf16", "uniform", "roundrobin"),
+    (333, 16, 64, 8, 8, "fp8", "uniform", "contiguous"),         # fp8, no scales
+    (200, 8192, 128, 2, 2, "bf16", "uniform", "contiguous"),     # 16 KiB rows
+    (90, 12288, 64, 3, 4, "bf16", "uniform", "contiguous"),      # rows above 16 KiB
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[f"M{c[0]}-N{c[1]}-G{c[2]}-k{c[3]}-B{c[4]}-{c[5]}-{c[6]}"
+                                            for c in EDGE])
+@pytest.mark.parametrize("dedup", [False, True])
+def test_edge_shapes(gpu_lib, case, dedup):
+    M, N, G, k, B, dtype, routing, bmap = case
+    w = wl.make_custom(M, N, G, k, B, dtype=dtype, routing=routing, bucket_map=bmap, seed=M)
+    if dtype == "fp8":
+        w.x_scale = None
+    ctx = f"{w.name} dedup={dedup}"
+    say(ctx)
+    ref = oracle.dispatch_layout(w.topk_idx, w.expert_bucket, w.B, dedup)
+    lay = gpu_layout(w, dedup)
+    assert_layout_equal(lay, ref, ctx)
+    out, out_scale = gpu_dispatch(w, lay)
+    assert_dispatch_equal(w, out, out_scale, ref, ctx=ctx)
+    if dtype == "bf16":
+        sent, _ = oracle.dispatch(w.x, ref.send_row, ref.R)
+        eo_ref = oracle.expert_outputs("identity", sent, ref.send_row, ref.slot, w.topk_idx)
+        y_ref = oracle.combine(eo_ref, w.weights, ref.slot)
+        eo = gpu_expert_outputs(w, lay, out, out_scale)
+        y = gpu_combine(w, lay, eo)
+        torch.cuda.synchronize()
+        assert_bits_equal(host(y), y_ref, ctx)
+
+
+def test_empty_batch(gpu_lib):
+    from combine_dispatch_layout_amd import moedl
+    idx = torch.empty((0, 8), dtype=torch.int32, device="cuda")
+    ebkt = dev((np.arange(256) // 32).astype(np.int32))
+    for dedup in (False, True):
+        lay = moedl.moe_dispatch_layout(idx, ebkt, 8, dedup)
+        torch.cuda.synchronize()
+        assert int(lay.status.item()) == 0
+        assert int(lay.expert_count.abs().sum().item()) == 0
+        assert int(lay.expert_offset.abs().sum().item()) == 0
+        assert host(lay.bucket_offset).tolist() == [0] * 9
+        x = torch.empty((0, 7168), dtype=torch.int16, device="cuda")
+        out, _ = moedl.moe_dispatch(x, lay.send_row, 0)
+        y = moedl.moe_combine(out, torch.empty((0, 8), dtype=torch.float32, device="cuda"),
+                              lay.slot)
+        torch.cuda.synchronize()
+        assert y.shape == (0, 7168)
+
+
+@pytest.mark.parametrize("dedup", [False, True])
+def test_bad_ids_status(gpu_lib, dedup):
+    w = wl.make_custom(600, 64, 32, 4, 4, seed=3)
+    idx = w.topk_idx.copy()
+    idx[300, 2] = 32            # first bad entry: flat 1202
+    idx[511, 0] = -5
+    w.topk_idx = idx
+    ref = oracle.dispatch_layout(idx, w.expert_bucket, w.B, dedup)
+    assert ref.status == 300 * 4 + 2 + 1
+    lay = gpu_layout(w, dedup)
+    assert_layout_equal(lay, ref, "bad ids")
+    # the erroneous layout must still be safe to dispatch and combine with
+    out, _ = gpu_dispatch(w, lay)
+    gpu_combine(w, lay, out)
+    torch.cuda.synchronize()
+    ebkt = w.expert_bucket.copy()
+    ebkt[7] = 4
+    w.expert_bucket = ebkt
+    lay = gpu_layout(w, dedup)
+    torch.cuda.synchronize()
+    assert int(lay.status.item()) == -8
+
+
+def test_deterministic_and_stream_ordered(gpu_lib):
+    w = wl.make_workload(3, M=2048)
+    results = []
+    for _ in range(2):
+        lay = gpu_layout(w, False)
+        out, _ = gpu_dispatch(w, lay)
+        y = gpu_combine(w, lay, out)
+        results.append([host(lay.slot), host(out), host(y)])
+    for a, b in zip(*results):
+        assert np.array_equal(a, b)
+    # on a side stream, with the inputs produced on that stream
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        lay = gpu_layout(w, False)
+        out, _ = gpu_dispatch(w, lay)
+        y = gpu_combine(w, lay, out)
+    s.synchronize()
+    assert np.array_equal(host(y), results[0][2])
