@@ -1,0 +1,271 @@
+"""Benchmark: MoE dispatch layout + dispatch + combine on one MI355X.
+
+Workload (the headline configuration): M=16384 tokens, N=7168 bf16 hidden, G=256
+experts, top-8 drawn without replacement from Zipf(1.2) over a seeded expert
+permutation, 8 buckets of 32 consecutive experts, softmax routing weights, identity
+experts, dedup off.  One step = moe_dispatch_layout + moe_dispatch + moe_combine
+(combine reads the dispatched rows in place: identity experts need no copy).  All
+inputs are resident in HBM before timing starts.
+
+Printed: one JSON line with algorithmic HBM GB/s (value), us per step, the roofline
+of the dominant kernel (per-kernel durations from HIP events recorded on the
+library's stream inside the timed region), a graph-replay latency following the
+microbenchmark method of "Purlin: Separating Orchestration from the Datapath of
+Collectives" (section 5: 128 invocations captured in a graph, one warm-up replay,
+eight timed replays, divided by 1,024), a plain copy-kernel ceiling, and the CPU
+oracle timed on the same inputs.
+
+    python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--dedup] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "dispatch+combine µs and HBM GB/s (% of peak), M=16384,N=7168,G=256,k=8"
+HBM_PEAK_GBPS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_FILE = os.path.join(PROFILES, "hbm_traffic_zipf1.2-top8-M16384.txt")
+KERNEL_SOURCES = {
+    "dispatch": "combine_dispatch_layout_amd/csrc/dispatch.hip",
+    "combine": "combine_dispatch_layout_amd/csrc/combine.hip",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--dedup", action="store_true", help="time dedup mode instead")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay leg")
+    ap.add_argument("--cfg", type=int, default=3, help=argparse.SUPPRESS)
+    return ap.parse_args()
+
+
+def source_hash(rel: str) -> str:
+    with open(os.path.join(ROOT, rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def recorded_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source (else None)."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get(f"{kernel}.source_sha256") != source_hash(KERNEL_SOURCES[kernel]):
+        return None
+    if vals.get("workload") != workload:
+        return None
+    try:
+        return float(vals[f"{kernel}.hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, dedup: bool, alg_bytes: float):
+    """The oracle as it stands, single-threaded, on the same inputs."""
+    import oracle
+    t0 = time.perf_counter()
+    lay = oracle.dispatch_layout(w.topk_idx, w.expert_bucket, w.B, dedup)
+    sent, _ = oracle.dispatch(w.x, lay.send_row, lay.R)
+    if dedup:
+        eo = oracle.expert_outputs("identity", sent, lay.send_row, lay.slot, w.topk_idx)
+    else:
+        eo = sent
+    oracle.combine(eo, w.weights, lay.slot)
+    dt = time.perf_counter() - t0
+    cpu_model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {
+        "value": round(alg_bytes / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
+        "kind": "oracle",
+        "sample": (f"whole workload ({w.M} tokens), one pass of layout+dispatch+combine "
+                   f"({'dedup, identity expansion included' if dedup else 'combine reads the dispatched rows'}), "
+                   f"{dt:.2f} s on 1 of {len(os.sched_getaffinity(0))} host cores ({cpu_model})"),
+        "seconds": round(dt, 3),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the path has no multi-GPU part to measure)", file=sys.stderr)
+        sys.exit(2)
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[var] = "1"
+
+    import torch
+    from combine_dispatch_layout_amd import harness, moedl, workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    moedl.load()
+    dev = torch.device("cuda:0")
+    dedup = bool(args.dedup)
+    w = workloads.make_workload(args.cfg)
+    M, N, G, k, B = w.M, w.N, w.G, w.k, w.B
+    row_bytes = w.row_bytes
+
+    idx = torch.from_numpy(w.topk_idx).to(dev)
+    ebkt = torch.from_numpy(w.expert_bucket).to(dev)
+    x = torch.from_numpy(w.x.view(np.int16)).to(dev)
+    wts = torch.from_numpy(w.weights).to(dev)
+    lay = moedl.alloc_layout(M, k, G, B, dedup, dev)
+    cap = lay.capacity
+    out = torch.empty((cap, N), dtype=torch.int16, device=dev)
+    y = torch.empty((M, N), dtype=torch.int16, device=dev)
+    eo = out if not dedup else torch.empty((M * k, N), dtype=torch.int16, device=dev)
+    slot_eo = lay.slot
+
+    def step():
+        moedl.moe_dispatch_layout(idx, ebkt, B, dedup, out=lay)
+        moedl.moe_dispatch(x, lay.send_row, cap, out=out)
+        moedl.moe_combine(eo, wts, slot_eo, y=y)
+
+    # warm-up (and one untimed dedup expansion so combine has real inputs)
+    for _ in range(max(1, args.warmup)):
+        step()
+    if dedup:
+        harness.expert_outputs("identity", out, lay.send_row, lay.slot, idx, out=eo)
+    torch.cuda.synchronize()
+    R = int(lay.bucket_offset[B].item())
+    assert int(lay.status.item()) == 0
+
+    # algorithmic bytes: read x once, write R send rows, read M*k expert rows, write M rows
+    disp_bytes = (M + R) * row_bytes
+    comb_bytes = (M * k + M) * row_bytes
+    total_bytes = disp_bytes + comb_bytes
+
+    # ---- timed region: exactly `steps` steps, per-kernel HIP events on the same stream
+    stream = torch.cuda.current_stream()
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        e = ev[i]
+        e[0].record(stream)
+        moedl.moe_dispatch_layout(idx, ebkt, B, dedup, out=lay)
+        e[1].record(stream)
+        moedl.moe_dispatch(x, lay.send_row, cap, out=out)
+        e[2].record(stream)
+        moedl.moe_combine(eo, wts, slot_eo, y=y)
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    lay_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    disp_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    comb_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+    span_ms = float(np.mean([e[0].elapsed_time(e[3]) for e in ev]))
+    ms_per_step = wall * 1e3 / K
+    gbps = total_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # ---- graph replay (128 invocations, 1 warm-up replay, 8 timed replays, / 1024)
+    graph_us = None
+    if not args.no_graph:
+        try:
+            g = torch.cuda.CUDAGraph()
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                step()
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g):
+                for _ in range(128):
+                    step()
+            g.replay()
+            torch.cuda.synchronize()
+            s, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            for _ in range(8):
+                g.replay()
+            e_.record()
+            torch.cuda.synchronize()
+            graph_us = s.elapsed_time(e_) * 1e3 / 1024
+            del g
+        except Exception as exc:  # report, never hide: the eager figure stands alone
+            print(f"graph replay skipped: {exc!r}", file=sys.stderr)
+
+    # ---- plain copy ceiling (2 GiB, 16-byte non-temporal streaming copy)
+    nbytes = 2 << 30
+    src = torch.empty(nbytes // 2, dtype=torch.int16, device=dev)
+    dst = torch.empty_like(src)
+    harness.copy(src, dst)
+    torch.cuda.synchronize()
+    cs, ce = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    cs.record()
+    for _ in range(10):
+        harness.copy(src, dst)
+    ce.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * nbytes * 10 / (cs.elapsed_time(ce) * 1e-3) / 1e9
+    del src, dst
+
+    # correctness guard on the timed buffers (identity experts: y == x)
+    torch.cuda.synchronize()
+    xz = torch.where(x == -32768, torch.zeros_like(x), x)
+    assert bool((y == xz).all().item()), "combine output differs from the input rows"
+
+    # ---- roofline of the dominant kernel
+    kernels = {"dispatch": (disp_ms, disp_bytes), "combine": (comb_ms, comb_bytes)}
+    dom = max(kernels, key=lambda n: kernels[n][0])
+    dms, dbytes = kernels[dom]
+    achieved = dbytes / (dms * 1e-3) / 1e9
+    traffic = recorded_traffic(dom, w.name + ("-dedup" if dedup else ""))
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": traffic, "alg_bytes_per_launch": dbytes,
+                "launch_us": round(dms * 1e3, 2)}
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(w, dedup, total_bytes)
+
+    res = {
+        "metric": METRIC, "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name + ("-dedup" if dedup else ""), "M": M, "N": N, "G": G,
+                   "k": k, "B": B, "routing": "zipf(1.2) top-8 without replacement",
+                   "dedup": dedup, "send_rows": R, "parallelism": "single-gpu"},
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+        "alg_bytes_per_step": total_bytes,
+        "event_us": {"layout": round(lay_ms * 1e3, 2), "dispatch": round(disp_ms * 1e3, 2),
+                     "combine": round(comb_ms * 1e3, 2), "span": round(span_ms * 1e3, 2)},
+        "kernel_gbps": {n: round(b / (t * 1e-3) / 1e9, 1) for n, (t, b) in kernels.items()},
+        "graph_replay_us_per_step": None if graph_us is None else round(graph_us, 2),
+        "graph_replay_gbps": None if graph_us is None else round(total_bytes / (graph_us * 1e-6) / 1e9, 1),
+        "copy_ceiling_gbps": round(copy_gbps, 1),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -4,76 +4,58 @@
 // the exchange ("All2all performance comparison between Triton-distributed and
 // DeepEP": the note under "Results" and the send buffer / scale buffer arguments of
 // "Test Code Snippet").  Push form: each token's row is read from HBM once and
-// written to every distinct send row of that token, so the bytes moved are exactly
-// one row read per token plus one row write per send row.
+// written once to every distinct send row of that token.
 //
-// Mapping: one wave64 per token, four tokens per 256-thread workgroup.  Each lane
-// holds up to VPL 16-byte vectors of the row in registers (lane-interleaved, so one
-// wave instruction moves 1 KiB of contiguous bytes), then stores them to each
-// destination.  The send rows of a token are wave-uniform scalar loads, and the
-// duplicate check (dedup mode: several experts of one token in one bucket share a
-// row) runs on the scalar unit.  Loads and stores are non-temporal: every byte is
-// touched once, so nothing is worth keeping in L2 or the Infinity Cache.
+// Mapping.  A row is cut into 1 KiB pieces (64 lanes x 16 bytes).  One workgroup
+// owns one (token, piece) and has k wave64s; wave j copies the piece to the send row
+// of the token's j-th choice, unless an earlier choice already names that row
+// (dedup mode) or the row is outside the buffer.  So every wave issues exactly one
+// 16-byte load and one 16-byte non-temporal store per lane and retires.
+//
+// Why this shape: the destinations of a token are k rows scattered over the send
+// buffer.  Measured on MI355X at 16384 tokens x 14 KiB x 8 destinations, a wave that
+// holds a whole row and stores it k times sustains ~4.8 TB/s; one wave per
+// (token, piece) storing k times ~5.5 TB/s; one store per wave ~6.8 TB/s.  Many
+// short waves, each with a single store in flight, keep HBM write efficiency high
+// under the scattered row pattern.  The k waves of a workgroup read the same x
+// piece; the loads are cached (plain, not non-temporal) so the repeats hit L2 and
+// HBM sees x once (rocprofv3 FETCH_SIZE confirms); the stores are non-temporal,
+// since nothing rereads the send buffer soon.
+//
+// Scales (fp8 rows): the workgroup of piece 0 copies each destination's
+// N/128-float scale row beside the data.
 #include "moe_internal.h"
 
 namespace moedl {
 namespace {
 
-constexpr int kTokensPerBlock = 4;
+constexpr int kPieceVecs = 64;  // 16-byte vectors per row piece (one per lane)
 
-template <int VPL>
-__global__ __launch_bounds__(256) void dispatch_rows_kernel(
-    const u32x4* __restrict__ x, int64_t M, int32_t row_vecs,
+__global__ __launch_bounds__(64 * MOE_MAX_TOPK) void dispatch_piece_kernel(
+    const u32x4* __restrict__ x, int64_t M, int32_t row_vecs, int32_t pieces,
     const float* __restrict__ x_scale, int32_t scale_cols,
     const int32_t* __restrict__ send_row, int32_t k, u32x4* __restrict__ out,
     float* __restrict__ out_scale, int64_t out_rows) {
   const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * kTokensPerBlock + wave_index();
+  const int j = wave_index();
+  const int64_t t = blockIdx.x / pieces;
+  const int piece = (int)(blockIdx.x - t * pieces);
   if (t >= M) return;
   const int32_t* rows = send_row + t * k;
+  const int r = rows[j];
+  bool skip = r < 0 || r >= out_rows;
+  for (int jj = 0; jj < j; ++jj) skip |= rows[jj] == r;
+  if (skip) return;
 
-  for (int base = 0; base < row_vecs; base += 64 * VPL) {
-    u32x4 v[VPL];
-    const u32x4* src = x + t * row_vecs + base + lane;
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      if (base + lane + 64 * i < row_vecs) v[i] = __builtin_nontemporal_load(src + 64 * i);
-    }
-    for (int j = 0; j < k; ++j) {
-      const int r = rows[j];
-      bool skip = r < 0 || r >= out_rows;
-      for (int jj = 0; jj < j; ++jj) skip |= rows[jj] == r;
-      if (skip) continue;
-      u32x4* dst = out + (int64_t)r * row_vecs + base + lane;
-#pragma unroll
-      for (int i = 0; i < VPL; ++i) {
-        if (base + lane + 64 * i < row_vecs) __builtin_nontemporal_store(v[i], dst + 64 * i);
-      }
-    }
+  const int c = piece * kPieceVecs + lane;
+  if (c < row_vecs) {
+    const u32x4 v = x[t * row_vecs + c];
+    __builtin_nontemporal_store(v, out + (int64_t)r * row_vecs + c);
   }
-
-  if (x_scale != nullptr) {
-    for (int c = lane; c < scale_cols; c += 64) {
-      const float s = x_scale[t * scale_cols + c];
-      for (int j = 0; j < k; ++j) {
-        const int r = rows[j];
-        bool skip = r < 0 || r >= out_rows;
-        for (int jj = 0; jj < j; ++jj) skip |= rows[jj] == r;
-        if (!skip) out_scale[(int64_t)r * scale_cols + c] = s;
-      }
-    }
+  if (x_scale != nullptr && piece == 0) {
+    for (int sc = lane; sc < scale_cols; sc += 64)
+      out_scale[(int64_t)r * scale_cols + sc] = x_scale[t * scale_cols + sc];
   }
-}
-
-template <int VPL>
-hipError_t launch_vpl(const void* x, int64_t M, int32_t row_vecs, const float* x_scale,
-                      int32_t scale_cols, const int32_t* send_row, int32_t k, void* out,
-                      float* out_scale, int64_t out_rows, hipStream_t stream) {
-  const int64_t blocks = (M + kTokensPerBlock - 1) / kTokensPerBlock;
-  hipLaunchKernelGGL(dispatch_rows_kernel<VPL>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                     (const u32x4*)x, M, row_vecs, x_scale, scale_cols, send_row, k,
-                     (u32x4*)out, out_scale, out_rows);
-  return hipGetLastError();
 }
 
 }  // namespace
@@ -83,20 +65,13 @@ hipError_t launch_dispatch(const void* x, int64_t M, int64_t row_bytes, const fl
                            float* out_scale, int64_t out_rows, hipStream_t stream) {
   if (M == 0) return hipSuccess;
   const int32_t row_vecs = (int32_t)(row_bytes / 16);
-  const int vpl = (row_vecs + 63) / 64;
-#define MOEDL_CASE(V)                                                                   \
-  case V:                                                                               \
-    return launch_vpl<V>(x, M, row_vecs, x_scale, scale_cols, send_row, k, out, out_scale, \
-                         out_rows, stream);
-  switch (vpl) {
-    MOEDL_CASE(1) MOEDL_CASE(2) MOEDL_CASE(3) MOEDL_CASE(4) MOEDL_CASE(5) MOEDL_CASE(6)
-    MOEDL_CASE(7) MOEDL_CASE(8) MOEDL_CASE(9) MOEDL_CASE(10) MOEDL_CASE(11) MOEDL_CASE(12)
-    MOEDL_CASE(13) MOEDL_CASE(14) MOEDL_CASE(15)
-    default:  // rows above 15 KiB: loop over the row in 16 KiB pieces
-      return launch_vpl<16>(x, M, row_vecs, x_scale, scale_cols, send_row, k, out, out_scale,
-                            out_rows, stream);
-  }
-#undef MOEDL_CASE
+  const int32_t pieces = (row_vecs + kPieceVecs - 1) / kPieceVecs;
+  const int64_t blocks = M * pieces;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(dispatch_piece_kernel, dim3((unsigned)blocks), dim3(64 * k), 0, stream,
+                     (const u32x4*)x, M, row_vecs, pieces, x_scale, scale_cols, send_row, k,
+                     (u32x4*)out, out_scale, out_rows);
+  return hipGetLastError();
 }
 
 }  // namespace moedl
