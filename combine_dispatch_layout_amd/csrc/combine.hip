@@ -10,17 +10,17 @@
 // fetched concurrently and consumed in source order.
 //
 // Mapping (LDS-staged).  A row is cut into 1 KiB pieces (64 lanes x 16 bytes = 512
-// bf16).  One workgroup owns one (token, piece) and has NW wave64s: wave w fetches
+// bf16).  One workgroup owns one (token, piece) and has NW = k/2 wave64s: wave w fetches
 // the piece of source rows j = w, w + NW, ... into LDS (one 16-byte non-temporal
 // load per lane per row), then wave 0 reads the k staged vectors back in j order,
 // accumulates in fp32 and stores the 16-byte bf16 result (non-temporal).
 //
 // Why this shape: measured on MI355X at 16384 tokens x 14 KiB x 8 sources, one wave
-// that loads all k sources of a piece and stores the result sustains ~6.0 TB/s;
-// spreading the k loads of the piece over 2 waves and joining them through LDS
-// ~6.3-6.5 TB/s (the loads of one piece issue from two wave slots, the store from
-// one).  The mix of scattered reads and a sequential write stream is what limits
-// HBM efficiency here; the arithmetic is hidden behind the loads.
+// that loads all k sources of a piece and stores the result sustains ~6.0 TB/s; the
+// same with k/2 waves of two loads each, joined through LDS, ~6.2 TB/s (1, 2 or 8
+// loading waves do no better).  A read-only pass over the same scattered rows runs
+// at ~6.9 TB/s: the mix of scattered reads with the output write stream is what
+// limits HBM efficiency here; the arithmetic is hidden behind the loads.
 #include "moe_internal.h"
 
 #pragma clang fp contract(off)
@@ -109,7 +109,7 @@ template <int K>
 hipError_t launch_k(const uint16_t* expert_out, int64_t expert_rows, const float* weights,
                     const int32_t* slot, int64_t M, int32_t row_vecs, uint16_t* y,
                     hipStream_t stream) {
-  constexpr int NW = K >= 4 ? K / 4 : 1;  // four source rows per wave
+  constexpr int NW = K >= 2 ? K / 2 : 1;  // two source rows per wave
   const int32_t pieces = (row_vecs + kPieceVecs - 1) / kPieceVecs;
   const int64_t blocks = M * pieces;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;

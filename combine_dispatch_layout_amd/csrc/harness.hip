@@ -69,11 +69,13 @@ __global__ __launch_bounds__(256) void standin_kernel(
   }
 }
 
+// One 16-byte vector per thread over a full grid: the fastest plain copy shape
+// measured on MI355X (~6.5 TB/s read+write at 2 GiB; a persistent grid-stride loop
+// reaches ~4.8 TB/s).
 __global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src,
                                                    u32x4* __restrict__ dst, int64_t n) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
-    __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
 }  // namespace
@@ -98,9 +100,9 @@ extern "C" int moe_harness_copy(const void* src, void* dst, size_t bytes, hipStr
   if (bytes % 16 != 0 || ((uintptr_t)src & 15u) || ((uintptr_t)dst & 15u)) return 1;
   if (bytes == 0) return 0;
   const int64_t n = (int64_t)(bytes / 16);
-  const int64_t want = (n + 255) / 256;
-  const unsigned blocks = (unsigned)(want < 256 * 16 ? want : 256 * 16);
-  hipLaunchKernelGGL(copy_kernel, dim3(blocks), dim3(256), 0, stream, (const u32x4*)src,
+  const int64_t blocks = (n + 255) / 256;
+  if (blocks > 0x7FFFFFFF) return 1;
+  hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (const u32x4*)src,
                      (u32x4*)dst, n);
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }

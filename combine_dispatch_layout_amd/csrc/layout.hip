@@ -36,6 +36,7 @@ constexpr int kMaxE = MOE_MAX_EXPERTS;
 constexpr int kMaxB = MOE_MAX_BUCKETS;
 constexpr int kMaxK = MOE_MAX_TOPK;
 constexpr unsigned char kBadBucket = 0xFF;
+constexpr int kAbsent = -1;  // no entry (past the end, or an invalid id)
 
 __device__ __forceinline__ int bits_for(int n) {  // bits needed for values in [0, n)
   return n <= 1 ? 0 : 32 - __builtin_clz((unsigned)(n - 1));
@@ -52,6 +53,7 @@ __device__ __forceinline__ uint64_t match_peers(bool ok, int key, int nbits) {
   return peers;
 }
 
+template <int KC>  // KC: k rounded up to a power of two (chunks per wave)
 __global__ __launch_bounds__(kTileThreads) void layout_tile_kernel(
     const int32_t* __restrict__ idx, int32_t M, int32_t k,
     const int32_t* __restrict__ ebkt, int32_t G, int32_t B, int32_t dedup,
@@ -60,6 +62,7 @@ __global__ __launch_bounds__(kTileThreads) void layout_tile_kernel(
     int32_t* __restrict__ tile_err) {
   __shared__ unsigned char map_s[kMaxE];
   __shared__ int32_t wcnt[kTileWaves][kMaxE];
+  __shared__ int32_t ids_s[kTileTokens * KC];  // the tile's expert ids, flat order
   __shared__ uint64_t wbal[kTileWaves][kMaxB];
   __shared__ int32_t wbcnt[kTileWaves][kMaxB];
   __shared__ int32_t err_s;
@@ -72,42 +75,46 @@ __global__ __launch_bounds__(kTileThreads) void layout_tile_kernel(
   const int nbits = bits_for(G);
   const uint64_t below = (1ull << lane) - 1ull;
 
-  if (tid == 0) err_s = kNoError;
+  // ---- all global loads first: KC chunks of 64 flat entries per wave.  Loads are
+  // unconditional (clamped index) so they are all in flight together.
+  const int64_t tbase = (int64_t)tile * kTileTokens * k;  // first flat entry of the tile
+  const int64_t wbase = tbase + (int64_t)w * 64 * k;
+  int ec[KC];
+#pragma unroll
+  for (int c = 0; c < KC; ++c) {
+    const int64_t f = wbase + (int64_t)c * 64 + lane;
+    const bool valid = c < k && f < Mk;
+    const int v = idx[valid ? f : 0];
+    ec[c] = valid ? v : kAbsent;
+  }
   for (int e = tid; e < G; e += kTileThreads) {
     const int b = ebkt[e];
     map_s[e] = (b >= 0 && b < B) ? (unsigned char)b : kBadBucket;
+#pragma unroll
+    for (int ww = 0; ww < kTileWaves; ++ww) wcnt[ww][e] = 0;
   }
-  for (int i = tid; i < kTileWaves * G; i += kTileThreads) wcnt[i / G][i % G] = 0;
+  if (tid == 0) err_s = kNoError;
   __syncthreads();
 
-  // ---- expert ranks: chunk c of wave w covers flat entries wbase + c*64 + lane
-  const int64_t wbase = ((int64_t)tile * kTileTokens + (int64_t)w * 64) * k;
-  int ec[kMaxK];
-  int rc[kMaxK];
+  // ---- stable ranks inside the wave: chunk c covers flat entries wbase + c*64 + lane
+  int rc[KC];
   int my_err = kNoError;
 #pragma unroll
-  for (int c = 0; c < kMaxK; ++c) {
-    ec[c] = -1;
-    rc[c] = 0;
-    if (c < k) {
-      const int64_t f = wbase + (int64_t)c * 64 + lane;
-      int e = -1;
-      if (f < Mk) {
-        e = idx[f];
-        if (e < 0 || e >= G) {
-          my_err = min(my_err, (int)f);
-          e = -1;
-        }
-      }
-      const bool ok = e >= 0;
-      const uint64_t peers = match_peers(ok, e, nbits);
-      const int r = lanes_below(peers);
-      int old = 0;
-      if (ok) old = wcnt[w][e];
-      if (ok && r == 0) wcnt[w][e] = old + __builtin_popcountll(peers);
-      ec[c] = e;
-      rc[c] = old + r;
+  for (int c = 0; c < KC; ++c) {
+    int e = ec[c];
+    if (e != kAbsent && (e < 0 || e >= G)) {
+      my_err = min(my_err, (int)(wbase + c * 64 + lane));
+      e = kAbsent;
     }
+    if (dedup && c < k) ids_s[w * 64 * k + c * 64 + lane] = e;
+    const bool ok = e >= 0;
+    const uint64_t peers = match_peers(ok, e, nbits);
+    const int r = lanes_below(peers);
+    int old = 0;
+    if (ok) old = wcnt[w][e];
+    if (ok && r == 0) wcnt[w][e] = old + __builtin_popcountll(peers);
+    ec[c] = e;
+    rc[c] = old + r;
   }
   if (my_err != kNoError) atomicMin(&err_s, my_err);
   __syncthreads();
@@ -125,25 +132,24 @@ __global__ __launch_bounds__(kTileThreads) void layout_tile_kernel(
   }
   __syncthreads();
 #pragma unroll
-  for (int c = 0; c < kMaxK; ++c) {
-    if (c < k) {
-      const int64_t f = wbase + (int64_t)c * 64 + lane;
-      if (f < Mk) slot_local[f] = ec[c] >= 0 ? wcnt[w][ec[c]] + rc[c] : -1;
-    }
+  for (int c = 0; c < KC; ++c) {
+    const int64_t f = wbase + (int64_t)c * 64 + lane;
+    if (c < k && f < Mk) slot_local[f] = ec[c] >= 0 ? wcnt[w][ec[c]] + rc[c] : -1;
   }
 
-  // ---- dedup rows: token view, lane = token
+  // ---- dedup rows: token view (lane = token), ids read back from LDS
   if (dedup) {
     const int64_t t = (int64_t)tile * kTileTokens + (int64_t)w * 64 + lane;
     const bool tv = t < M;
-    int eb[kMaxK];
+    const int* my_ids = ids_s + (w * 64 + lane) * k;
+    int eb[KC];
     uint64_t bmask = 0;
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
+    for (int j = 0; j < KC; ++j) {
       eb[j] = kBadBucket;
       if (j < k && tv) {
-        const int e = idx[t * k + j];
-        if (e >= 0 && e < G) {
+        const int e = my_ids[j];
+        if (e >= 0) {
           eb[j] = map_s[e];
           if (eb[j] != kBadBucket) bmask |= 1ull << eb[j];
         }
@@ -170,7 +176,7 @@ __global__ __launch_bounds__(kTileThreads) void layout_tile_kernel(
     __syncthreads();
     if (tv) {
 #pragma unroll
-      for (int j = 0; j < kMaxK; ++j) {
+      for (int j = 0; j < KC; ++j) {
         if (j < k) {
           const int b = eb[j];
           row_local[t * k + j] =
@@ -183,9 +189,13 @@ __global__ __launch_bounds__(kTileThreads) void layout_tile_kernel(
 }
 
 // Exclusive prefix down each column of data[T][C] (row-major), in place, using the
-// whole 1024-thread workgroup: P = 1024 / C threads share a column, each summing a
-// contiguous run of rows, and a short serial scan joins the runs.  totals[c] gets
-// the column sum.  seg must hold kScanThreads ints.
+// whole 1024-thread workgroup: P = 1024 / C threads share a column, each owning a
+// contiguous run of rows, and a short serial scan joins the runs.  Each thread
+// loads its run into registers once (kSegRegs rows per round trip), so a column of
+// up to P * kSegRegs tiles costs one global round trip.  totals[c] gets the column
+// sum.  seg must hold kScanThreads ints.
+constexpr int kSegRegs = 16;
+
 __device__ void column_exclusive_scan(int32_t* __restrict__ data, int T, int C,
                                       int32_t* totals, int32_t* seg) {
   const int tid = threadIdx.x;
@@ -194,49 +204,50 @@ __device__ void column_exclusive_scan(int32_t* __restrict__ data, int T, int C,
   const int col = tid % C;
   const int p = tid / C;
   const bool active = tid < P * C;
-  const int t0 = min(T, p * per);
-  const int t1 = min(T, t0 + per);
+  const int t0 = active ? min(T, p * per) : T;
+  const int t1 = active ? min(T, t0 + per) : T;
+  int v[kSegRegs];
   int sum = 0;
-  if (active) {
-    int t = t0;
-    for (; t + 8 <= t1; t += 8) {
-      int v[8];
+  // pass 1: segment sums (the last batch stays in registers)
+  for (int b0 = t0; b0 < t1; b0 += kSegRegs) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = data[(int64_t)(t + u) * C + col];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) sum += v[u];
+    for (int u = 0; u < kSegRegs; ++u) {
+      const int t = b0 + u;
+      v[u] = t < t1 ? data[(int64_t)t * C + col] : 0;
     }
-    for (; t < t1; ++t) sum += data[(int64_t)t * C + col];
-    seg[p * C + col] = sum;
+#pragma unroll
+    for (int u = 0; u < kSegRegs; ++u) sum += v[u];
   }
+  if (active) seg[p * C + col] = sum;
   __syncthreads();
   if (tid < C) {
     int run = 0;
     for (int q = 0; q < P; ++q) {
-      const int v = seg[q * C + tid];
+      const int x = seg[q * C + tid];
       seg[q * C + tid] = run;
-      run += v;
+      run += x;
     }
     totals[tid] = run;
   }
   __syncthreads();
+  // pass 2: prefixes; a segment of one batch is still in registers
   if (active) {
     int run = seg[p * C + col];
-    int t = t0;
-    for (; t + 8 <= t1; t += 8) {
-      int v[8];
+    if (t1 - t0 <= kSegRegs) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = data[(int64_t)(t + u) * C + col];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        data[(int64_t)(t + u) * C + col] = run;
-        run += v[u];
+      for (int u = 0; u < kSegRegs; ++u) {
+        const int t = t0 + u;
+        if (t < t1) {
+          data[(int64_t)t * C + col] = run;
+          run += v[u];
+        }
       }
-    }
-    for (; t < t1; ++t) {
-      const int v = data[(int64_t)t * C + col];
-      data[(int64_t)t * C + col] = run;
-      run += v;
+    } else {
+      for (int t = t0; t < t1; ++t) {
+        const int x = data[(int64_t)t * C + col];
+        data[(int64_t)t * C + col] = run;
+        run += x;
+      }
     }
   }
   __syncthreads();
@@ -297,20 +308,22 @@ __global__ __launch_bounds__(kScanThreads) void layout_scan_kernel(
   if (tid < kMaxB) bsum_s[tid] = 0;
   __syncthreads();
 
-  // status: bad map entries first, then the first bad expert id
-  for (int i = tid; i < T; i += kScanThreads) {
-    const int e = tile_err[i];
-    if (e != kNoError) atomicMin(&err_s, e);
-  }
-  int b_of_e = 0;
-  if (tid < G) {
-    const int b = ebkt[tid];
-    if (b < 0 || b >= B) atomicMin(&mapbad_s, tid);
-    b_of_e = min(max(b, 0), B - 1);
-  }
+  // Issue the small loads first; they are consumed after the column scan has issued
+  // its own, so all global reads of this kernel share one round trip.
+  const int map_b = tid < G ? ebkt[tid] : 0;
+  int terr = kNoError;
+  for (int i = tid; i < T; i += kScanThreads) terr = min(terr, tile_err[i]);
 
   // per-expert counts: column scan of the tile histograms
   column_exclusive_scan(tile_hist, T, G, cnt_s, seg);
+
+  // status: bad map entries first, then the first bad expert id
+  if (terr != kNoError) atomicMin(&err_s, terr);
+  int b_of_e = 0;
+  if (tid < G) {
+    if (map_b < 0 || map_b >= B) atomicMin(&mapbad_s, tid);
+    b_of_e = min(max(map_b, 0), B - 1);
+  }
 
   // memory order of experts: sigma = sorted by (bucket, id).  Rank inside the wave
   // among experts of the same bucket, then per-(wave, bucket) prefixes.
@@ -440,9 +453,16 @@ hipError_t launch_layout(const int32_t* topk_idx, int64_t M, int32_t k,
   const int T = (int)layout_tiles(M);
   const int64_t Mk = M * k;
   if (T > 0) {
-    hipLaunchKernelGGL(layout_tile_kernel, dim3(T), dim3(kTileThreads), 0, stream, topk_idx,
-                       (int32_t)M, k, expert_bucket, G, B, dedup, slot, send_row,
-                       ws.tile_hist, ws.tile_bhist, ws.tile_err);
+#define MOEDL_TILE(KC)                                                                        \
+  hipLaunchKernelGGL(layout_tile_kernel<KC>, dim3(T), dim3(kTileThreads), 0, stream, topk_idx, \
+                     (int32_t)M, k, expert_bucket, G, B, dedup, slot, send_row, ws.tile_hist,  \
+                     ws.tile_bhist, ws.tile_err)
+    if (k <= 1) MOEDL_TILE(1);
+    else if (k <= 2) MOEDL_TILE(2);
+    else if (k <= 4) MOEDL_TILE(4);
+    else if (k <= 8) MOEDL_TILE(8);
+    else MOEDL_TILE(16);
+#undef MOEDL_TILE
   }
   hipLaunchKernelGGL(layout_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, T, G, B, dedup,
                      expert_bucket, ws.tile_hist, ws.tile_bhist, ws.tile_err, expert_count,
