@@ -79,9 +79,9 @@ size_t moe_dispatch_layout_workspace_bytes(int64_t M, int32_t k, int32_t G, int3
  * Passages: the send buffer grouped by destination, its splits and cumulative sums
  * ("All2all performance comparison ...", "Test Code Snippet"); per-expert row
  * offsets that stay on the device for a grouped GEMM ("Add Triton grouped-GEMM for
- * MoE experts on Ampere/Ada", "What this PR does"); a token sent to a destination
- * only once however many of its experts live there ("Zyphra says routing-pattern
- * expert placement ...", the 58% copy-reduction item).
+ * MoE experts on Ampere/Ada", "What this PR does"); one copy per (token,
+ * destination) pair even when several of the token's experts share that destination
+ * ("Zyphra says routing-pattern expert placement ...", the 58% copy-reduction item).
  *
  * Inputs:
  *   topk_idx      int32 [M*k], row-major [M][k]: expert id of token t's j-th choice,

@@ -14,8 +14,8 @@ Sources (web pages, cited by title and section):
   their cumulative sums, optional per-row scales, hidden size, experts per rank and
   total experts; dispatch and combine as the two phases.
 * "Zyphra says routing-pattern expert placement speeds MoE token communication up to
-  2.63x on AMD MI300X": a token is sent to a destination once, however many of its
-  experts live there (dedup mode), under an arbitrary expert placement.
+  2.63x on AMD MI300X": a (token, destination) pair travels as one copy even when several
+  of the token's experts sit at that destination (dedup mode), under an arbitrary expert placement.
 * "Add Triton grouped-GEMM for MoE experts on Ampere/Ada" (DeepSpeed PR 8180),
   "What this PR does": per-expert row offsets ``offs`` that stay on the device.
 * "Purlin: Separating Orchestration from the Datapath of Collectives", section 3.3
