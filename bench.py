@@ -16,6 +16,8 @@ eight timed replays, divided by 1,024), a plain copy-kernel ceiling, and the CPU
 oracle timed on the same inputs.
 
     python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--dedup] [--no-cpu]
+    python bench.py --path bucket    # dedup round trip: layout, dispatch, moe_expand,
+                                     # moe_combine_partial, moe_combine_reduce
 """
 from __future__ import annotations
 
@@ -49,6 +51,8 @@ def parse():
     ap.add_argument("--dedup", action="store_true", help="time dedup mode instead")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay leg")
+    ap.add_argument("--path", choices=["flat", "bucket"], default="flat",
+                    help="flat: layout+dispatch+combine; bucket: the dedup round trip")
     ap.add_argument("--cfg", type=int, default=3, help=argparse.SUPPRESS)
     return ap.parse_args()
 
@@ -108,6 +112,70 @@ def cpu_baseline(w, dedup: bool, alg_bytes: float):
     }
 
 
+def bench_bucket(args, w, dev):
+    """Dedup round trip with identity experts: layout (dedup) -> dispatch -> expand ->
+    combine_partial -> combine_reduce.  Prints one JSON line (not the headline)."""
+    import torch
+    from combine_dispatch_layout_amd import moedl
+    M, N, G, k, B = w.M, w.N, w.G, w.k, w.B
+    rb = w.row_bytes
+    idx = torch.from_numpy(w.topk_idx).to(dev)
+    ebkt = torch.from_numpy(w.expert_bucket).to(dev)
+    x = torch.from_numpy(w.x.view(np.int16)).to(dev)
+    wts = torch.from_numpy(w.weights).to(dev)
+    lay = moedl.alloc_layout(M, k, G, B, True, dev)
+    cap = lay.capacity
+    out = torch.empty((cap, N), dtype=torch.int16, device=dev)
+    ein = torch.empty((M * k, N), dtype=torch.int16, device=dev)
+    part = torch.empty((cap, N), dtype=torch.int16, device=dev)
+    y = torch.empty((M, N), dtype=torch.int16, device=dev)
+    calls = [
+        lambda: moedl.moe_dispatch_layout(idx, ebkt, B, True, out=lay),
+        lambda: moedl.moe_dispatch(x, lay.send_row, cap, out=out, dedup=True),
+        lambda: moedl.moe_expand(out, lay.send_row, lay.slot, M * k, out=ein),
+        lambda: moedl.moe_combine_partial(ein, wts, lay.slot, lay.send_row, cap, partial=part),
+        lambda: moedl.moe_combine_reduce(part, lay.send_row, y=y),
+    ]
+    for _ in range(max(1, args.warmup)):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    assert int(lay.status.item()) == 0
+    R = int(lay.bucket_offset[B].item())
+    rows = {"layout": 0, "dispatch": M + R, "expand": R + M * k, "combine_partial": M * k + R,
+            "combine_reduce": R + M}
+    names = list(rows)
+    stream = torch.cuda.current_stream()
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        for c, e in zip(calls, ev[i][1:]):
+            c()
+            e.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {n: float(np.mean([e[q].elapsed_time(e[q + 1]) for e in ev])) for q, n in enumerate(names)}
+    total = sum(rows.values()) * rb
+    ms = wall * 1e3 / K
+    # identity experts, weights summing to one: y is x to within two bf16 roundings
+    diff = (y.view(torch.bfloat16).float() - x.view(torch.bfloat16).float()).abs()
+    assert bool((diff <= x.view(torch.bfloat16).float().abs() * (2 * 2.0 ** -8) + 1e-30).all().item())
+    res = {"metric": METRIC + " [dedup round trip]", "value": round(total / (ms * 1e-3) / 1e9, 1),
+           "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+           "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": w.name + "-dedup-roundtrip", "M": M, "N": N, "G": G, "k": k,
+                      "B": B, "send_rows": R, "dedup_saving": round(1 - R / (M * k), 4)},
+           "us_per_step": round(ms * 1e3, 2), "alg_bytes_per_step": total,
+           "event_us": {n: round(per[n] * 1e3, 2) for n in names},
+           "kernel_gbps": {n: round(rows[n] * rb / (per[n] * 1e-3) / 1e9, 1)
+                           for n in names if rows[n]}}
+    print(json.dumps(res))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -125,6 +193,9 @@ def main():
     dev = torch.device("cuda:0")
     dedup = bool(args.dedup)
     w = workloads.make_workload(args.cfg)
+    if args.path == "bucket":
+        bench_bucket(args, w, dev)
+        return
     M, N, G, k, B = w.M, w.N, w.G, w.k, w.B
     row_bytes = w.row_bytes
 
@@ -141,7 +212,7 @@ def main():
 
     def step():
         moedl.moe_dispatch_layout(idx, ebkt, B, dedup, out=lay)
-        moedl.moe_dispatch(x, lay.send_row, cap, out=out)
+        moedl.moe_dispatch(x, lay.send_row, cap, out=out, dedup=dedup)
         moedl.moe_combine(eo, wts, slot_eo, y=y)
 
     # warm-up (and one untimed dedup expansion so combine has real inputs)
@@ -169,7 +240,7 @@ def main():
         e[0].record(stream)
         moedl.moe_dispatch_layout(idx, ebkt, B, dedup, out=lay)
         e[1].record(stream)
-        moedl.moe_dispatch(x, lay.send_row, cap, out=out)
+        moedl.moe_dispatch(x, lay.send_row, cap, out=out, dedup=dedup)
         e[2].record(stream)
         moedl.moe_combine(eo, wts, slot_eo, y=y)
         e[3].record(stream)

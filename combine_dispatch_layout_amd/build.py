@@ -32,7 +32,7 @@ COMMON = [
 ]
 
 LIBS = {
-    "libmoedl.so": ["api.cpp", "layout.hip", "dispatch.hip", "combine.hip"],
+    "libmoedl.so": ["api.cpp", "layout.hip", "dispatch.hip", "combine.hip", "bucket.hip"],
     "libmoedl_harness.so": ["harness.hip"],
 }
 

@@ -7,7 +7,7 @@
 
 namespace {
 
-constexpr int32_t kAbiVersion = 1;
+constexpr int32_t kAbiVersion = 2;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -64,9 +64,10 @@ moe_status moe_dispatch_layout(const int32_t* topk_idx, int64_t M, int32_t k,
 }
 
 moe_status moe_dispatch(const void* x, moe_dtype dtype, int64_t M, int32_t N,
-                        const float* x_scale, const int32_t* send_row, int32_t k, void* out,
-                        float* out_scale, int64_t out_rows, hipStream_t stream) {
+                        const float* x_scale, const int32_t* send_row, int32_t k, int32_t dedup,
+                        void* out, float* out_scale, int64_t out_rows, hipStream_t stream) {
   if (M < 0 || N < 1 || k < 1 || out_rows < 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (dedup != 0 && dedup != 1) return MOE_ERR_INVALID_ARGUMENT;
   if (dtype != MOE_BF16 && dtype != MOE_FP8_E4M3) return MOE_ERR_INVALID_ARGUMENT;
   if (k > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
   if ((x_scale == nullptr) != (out_scale == nullptr)) return MOE_ERR_INVALID_ARGUMENT;
@@ -80,8 +81,8 @@ moe_status moe_dispatch(const void* x, moe_dtype dtype, int64_t M, int32_t N,
   if (x_scale && (((uintptr_t)x_scale & 3u) || ((uintptr_t)out_scale & 3u)))
     return MOE_ERR_INVALID_ARGUMENT;
   const int32_t scale_cols = x_scale ? N / MOE_SCALE_BLOCK : 0;
-  return from_hip(moedl::launch_dispatch(x, M, row_bytes, x_scale, scale_cols, send_row, k, out,
-                                         out_scale, out_rows, stream));
+  return from_hip(moedl::launch_dispatch(x, M, row_bytes, x_scale, scale_cols, send_row, k,
+                                         dedup, out, out_scale, out_rows, stream));
 }
 
 moe_status moe_combine(const uint16_t* expert_out, int64_t expert_rows, const float* weights,
@@ -95,6 +96,57 @@ moe_status moe_combine(const uint16_t* expert_out, int64_t expert_rows, const fl
     return MOE_ERR_INVALID_ARGUMENT;
   return from_hip(
       moedl::launch_combine(expert_out, expert_rows, weights, slot, M, k, N, y, stream));
+}
+
+moe_status moe_expand(const void* recv, moe_dtype dtype, int64_t recv_rows, int32_t N,
+                      const float* recv_scale, const int32_t* send_row, const int32_t* slot,
+                      int64_t M, int32_t k, void* expert_in, float* expert_scale,
+                      int64_t expert_rows, hipStream_t stream) {
+  if (M < 0 || N < 1 || k < 1 || recv_rows < 0 || expert_rows < 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (dtype != MOE_BF16 && dtype != MOE_FP8_E4M3) return MOE_ERR_INVALID_ARGUMENT;
+  if (k > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
+  if ((recv_scale == nullptr) != (expert_scale == nullptr)) return MOE_ERR_INVALID_ARGUMENT;
+  if (recv_scale && dtype != MOE_FP8_E4M3) return MOE_ERR_INVALID_ARGUMENT;
+  const int64_t row_bytes = (int64_t)N * (dtype == MOE_BF16 ? 2 : 1);
+  if (row_bytes % 16 != 0) return MOE_ERR_UNSUPPORTED;
+  if (recv_scale && N % MOE_SCALE_BLOCK != 0) return MOE_ERR_UNSUPPORTED;
+  if (M > 0 && (!send_row || !slot)) return MOE_ERR_INVALID_ARGUMENT;
+  if ((recv_rows > 0 && !recv) || (expert_rows > 0 && !expert_in)) return MOE_ERR_INVALID_ARGUMENT;
+  if ((recv && !aligned16(recv)) || (expert_in && !aligned16(expert_in)))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (recv_scale && (((uintptr_t)recv_scale & 3u) || ((uintptr_t)expert_scale & 3u)))
+    return MOE_ERR_INVALID_ARGUMENT;
+  const int32_t scale_cols = recv_scale ? N / MOE_SCALE_BLOCK : 0;
+  return from_hip(moedl::launch_expand(recv, recv_rows, row_bytes, recv_scale, scale_cols,
+                                       send_row, slot, M, k, expert_in, expert_scale,
+                                       expert_rows, stream));
+}
+
+moe_status moe_combine_partial(const uint16_t* expert_out, int64_t expert_rows,
+                               const float* weights, const int32_t* slot,
+                               const int32_t* send_row, int64_t M, int32_t k, int32_t N,
+                               uint16_t* partial, int64_t partial_rows, hipStream_t stream) {
+  if (M < 0 || N < 1 || k < 1 || expert_rows < 0 || partial_rows < 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (k > MOE_MAX_TOPK || N % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if (M > 0 && (!weights || !slot || !send_row)) return MOE_ERR_INVALID_ARGUMENT;
+  if ((expert_rows > 0 && !expert_out) || (partial_rows > 0 && !partial))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if ((expert_out && !aligned16(expert_out)) || (partial && !aligned16(partial)))
+    return MOE_ERR_INVALID_ARGUMENT;
+  return from_hip(moedl::launch_combine_partial(expert_out, expert_rows, weights, slot, send_row,
+                                                M, k, N, partial, partial_rows, stream));
+}
+
+moe_status moe_combine_reduce(const uint16_t* partial, int64_t partial_rows,
+                              const int32_t* send_row, int64_t M, int32_t k, int32_t N,
+                              uint16_t* y, hipStream_t stream) {
+  if (M < 0 || N < 1 || k < 1 || partial_rows < 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (k > MOE_MAX_TOPK || N % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if (M > 0 && (!send_row || !y)) return MOE_ERR_INVALID_ARGUMENT;
+  if (partial_rows > 0 && !partial) return MOE_ERR_INVALID_ARGUMENT;
+  if ((partial && !aligned16(partial)) || (y && !aligned16(y))) return MOE_ERR_INVALID_ARGUMENT;
+  return from_hip(
+      moedl::launch_combine_reduce(partial, partial_rows, send_row, M, k, N, y, stream));
 }
 
 }  // extern "C"

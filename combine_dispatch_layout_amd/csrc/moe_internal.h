@@ -39,12 +39,26 @@ hipError_t launch_layout(const int32_t* topk_idx, int64_t M, int32_t k,
 
 hipError_t launch_dispatch(const void* x, int64_t M, int64_t row_bytes,
                            const float* x_scale, int32_t scale_cols,
-                           const int32_t* send_row, int32_t k, void* out,
+                           const int32_t* send_row, int32_t k, int32_t dedup, void* out,
                            float* out_scale, int64_t out_rows, hipStream_t stream);
 
 hipError_t launch_combine(const uint16_t* expert_out, int64_t expert_rows,
                           const float* weights, const int32_t* slot, int64_t M,
                           int32_t k, int32_t N, uint16_t* y, hipStream_t stream);
+
+hipError_t launch_expand(const void* recv, int64_t recv_rows, int64_t row_bytes,
+                         const float* recv_scale, int32_t scale_cols, const int32_t* send_row,
+                         const int32_t* slot, int64_t M, int32_t k, void* expert_in,
+                         float* expert_scale, int64_t expert_rows, hipStream_t stream);
+
+hipError_t launch_combine_partial(const uint16_t* expert_out, int64_t expert_rows,
+                                  const float* weights, const int32_t* slot,
+                                  const int32_t* send_row, int64_t M, int32_t k, int32_t N,
+                                  uint16_t* partial, int64_t partial_rows, hipStream_t stream);
+
+hipError_t launch_combine_reduce(const uint16_t* partial, int64_t partial_rows,
+                                 const int32_t* send_row, int64_t M, int32_t k, int32_t N,
+                                 uint16_t* y, hipStream_t stream);
 
 // ---------------------------------------------------------------- device helpers
 #if defined(__HIP_DEVICE_COMPILE__) || defined(__HIPCC__)

@@ -42,8 +42,13 @@ SIGNATURES = {
         _i32p, _i64, _i32, _i32p, _i32, _i32, _i32, _i32p, _i32p, _i32p, _i32p, _i32p,
         _i32p, _i32p, _i32p, _vp, ctypes.c_size_t, _vp]),
     "moe_dispatch": (ctypes.c_int, [
-        _vp, ctypes.c_int, _i64, _i32, _vp, _i32p, _i32, _vp, _vp, _i64, _vp]),
+        _vp, ctypes.c_int, _i64, _i32, _vp, _i32p, _i32, _i32, _vp, _vp, _i64, _vp]),
     "moe_combine": (ctypes.c_int, [_vp, _i64, _vp, _i32p, _i64, _i32, _i32, _vp, _vp]),
+    "moe_expand": (ctypes.c_int, [
+        _vp, ctypes.c_int, _i64, _i32, _vp, _i32p, _i32p, _i64, _i32, _vp, _vp, _i64, _vp]),
+    "moe_combine_partial": (ctypes.c_int, [
+        _vp, _i64, _vp, _i32p, _i32p, _i64, _i32, _i32, _vp, _i64, _vp]),
+    "moe_combine_reduce": (ctypes.c_int, [_vp, _i64, _i32p, _i64, _i32, _i32, _vp, _vp]),
 }
 
 
@@ -161,9 +166,10 @@ def _dtype_code(x: torch.Tensor) -> int:
 
 def moe_dispatch(x: torch.Tensor, send_row: torch.Tensor, out_rows: int,
                  x_scale: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-                 out_scale: Optional[torch.Tensor] = None, stream=None):
+                 out_scale: Optional[torch.Tensor] = None, dedup: bool = False, stream=None):
     """x [M, N] (bf16 bits or fp8 codes), send_row int32 [M, k] -> (out [out_rows, N],
-    out_scale [out_rows, N/128] or None)."""
+    out_scale [out_rows, N/128] or None).  dedup: send_row came from a dedup layout
+    (selects the kernel shape only)."""
     M, N = x.shape
     k = send_row.shape[1] if send_row.dim() == 2 else 1
     if out is None:
@@ -172,7 +178,7 @@ def moe_dispatch(x: torch.Tensor, send_row: torch.Tensor, out_rows: int,
         out_scale = torch.empty((out_rows, x_scale.shape[1]), dtype=torch.float32,
                                 device=x.device)
     st = lib().moe_dispatch(_ptr(x), _dtype_code(x), M, N, _ptr(x_scale), _ptr(send_row), k,
-                            _ptr(out), _ptr(out_scale), out_rows, _stream(stream))
+                            int(dedup), _ptr(out), _ptr(out_scale), out_rows, _stream(stream))
     _check("moe_dispatch", st)
     return out, out_scale
 
@@ -189,4 +195,50 @@ def moe_combine(expert_out: torch.Tensor, weights: torch.Tensor, slot: torch.Ten
     st = lib().moe_combine(_ptr(expert_out), rows, _ptr(weights), _ptr(slot), M, k, N, _ptr(y),
                            _stream(stream))
     _check("moe_combine", st)
+    return y
+
+
+def moe_expand(recv: torch.Tensor, send_row: torch.Tensor, slot: torch.Tensor, expert_rows: int,
+               recv_scale: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+               out_scale: Optional[torch.Tensor] = None, stream=None):
+    """Receiver-side expansion: out[slot[t, j]] = recv[send_row[t, j]] (+ scales)."""
+    R, N = recv.shape
+    M, k = slot.shape
+    if out is None:
+        out = torch.empty((expert_rows, N), dtype=recv.dtype, device=recv.device)
+    if recv_scale is not None and out_scale is None:
+        out_scale = torch.empty((expert_rows, recv_scale.shape[1]), dtype=torch.float32,
+                                device=recv.device)
+    st = lib().moe_expand(_ptr(recv), _dtype_code(recv), R, N, _ptr(recv_scale), _ptr(send_row),
+                          _ptr(slot), M, k, _ptr(out), _ptr(out_scale), expert_rows,
+                          _stream(stream))
+    _check("moe_expand", st)
+    return out, out_scale
+
+
+def moe_combine_partial(expert_out: torch.Tensor, weights: torch.Tensor, slot: torch.Tensor,
+                        send_row: torch.Tensor, partial_rows: int,
+                        partial: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Per-(token, bucket) partial sums, bf16 [partial_rows, N]."""
+    rows, N = expert_out.shape
+    M, k = slot.shape
+    if partial is None:
+        partial = torch.empty((partial_rows, N), dtype=expert_out.dtype, device=expert_out.device)
+    st = lib().moe_combine_partial(_ptr(expert_out), rows, _ptr(weights), _ptr(slot),
+                                   _ptr(send_row), M, k, N, _ptr(partial), partial_rows,
+                                   _stream(stream))
+    _check("moe_combine_partial", st)
+    return partial
+
+
+def moe_combine_reduce(partial: torch.Tensor, send_row: torch.Tensor,
+                       y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """y[t] = bf16(sum of the token's distinct partial rows, ascending)."""
+    rows, N = partial.shape
+    M, k = send_row.shape
+    if y is None:
+        y = torch.empty((M, N), dtype=partial.dtype, device=partial.device)
+    st = lib().moe_combine_reduce(_ptr(partial), rows, _ptr(send_row), M, k, N, _ptr(y),
+                                  _stream(stream))
+    _check("moe_combine_reduce", st)
     return y

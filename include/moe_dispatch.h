@@ -137,18 +137,21 @@ moe_status moe_dispatch_layout(const int32_t* topk_idx, int64_t M, int32_t k,
  *   x_scale   float [M, N/128] or NULL.  Only with MOE_FP8_E4M3, and then
  *             N % 128 == 0.
  *   send_row  int32 [M*k] from moe_dispatch_layout (any map into rows works).
+ *   dedup     0 or 1: whether send_row came from a dedup layout.  Only selects the
+ *             kernel shape (k single-store waves per row piece, or two waves sharing
+ *             the token's distinct rows); the bytes written are the same.
  * Outputs:
  *   out       [out_rows, N] elements of `dtype`; rows named by send_row are written.
  *   out_scale float [out_rows, N/128]; NULL exactly when x_scale is NULL.
  *   out_rows  capacity of out in rows.  Entries of send_row outside [0, out_rows)
  *             are skipped, so an erroneous layout can never write out of bounds.
  * Errors: MOE_ERR_INVALID_ARGUMENT (null or misaligned pointers, M < 0, N < 1,
- * k < 1, scales with bf16, out_scale/x_scale mismatch), MOE_ERR_UNSUPPORTED (row
+ * k < 1, dedup not 0/1, scales with bf16, out_scale/x_scale mismatch), MOE_ERR_UNSUPPORTED (row
  * bytes not a multiple of 16, scales with N % 128 != 0, k > 16), MOE_ERR_LAUNCH.
  */
 moe_status moe_dispatch(const void* x, moe_dtype dtype, int64_t M, int32_t N,
                         const float* x_scale, const int32_t* send_row, int32_t k,
-                        void* out, float* out_scale, int64_t out_rows,
+                        int32_t dedup, void* out, float* out_scale, int64_t out_rows,
                         hipStream_t stream);
 
 /*
@@ -177,6 +180,71 @@ moe_status moe_dispatch(const void* x, moe_dtype dtype, int64_t M, int32_t N,
 moe_status moe_combine(const uint16_t* expert_out, int64_t expert_rows,
                        const float* weights, const int32_t* slot, int64_t M, int32_t k,
                        int32_t N, uint16_t* y, hipStream_t stream);
+
+/*
+ * ---------------------------------------------------------------------------------
+ * The steps on either side of the path in dedup mode.  A (token, bucket) pair
+ * travels as one row ("Zyphra says routing-pattern expert placement ...", the
+ * copy-reduction item); the receiver turns it back into one row per expert, and on
+ * the way back the token's experts inside a bucket are summed before the return, so
+ * one row per (token, bucket) travels instead of one per (token, j).  The return path
+ * is not described on the pages; this is its mirror image of the forward path.
+ * ---------------------------------------------------------------------------------
+ */
+
+/*
+ * moe_expand -- receiver-side expansion:  expert_in[slot[f]] = recv[send_row[f]] for
+ * every entry f = t*k + j (raw bytes, scales follow the rows).
+ *
+ *   recv        [recv_rows, N] elements of `dtype` (a dedup send buffer, or what the
+ *               exchange delivered), 16-byte aligned.
+ *   recv_scale  float [recv_rows, N/128] or NULL (fp8 only).
+ *   send_row, slot  int32 [M*k] from moe_dispatch_layout (dedup = 1).
+ *   expert_in   [expert_rows, N] of `dtype`, slot-indexed; expert_scale float
+ *               [expert_rows, N/128], NULL exactly when recv_scale is NULL.
+ * Entries whose send row or slot is out of range are skipped.
+ * Errors: as moe_dispatch (argument checks on the host).
+ */
+moe_status moe_expand(const void* recv, moe_dtype dtype, int64_t recv_rows, int32_t N,
+                      const float* recv_scale, const int32_t* send_row, const int32_t* slot,
+                      int64_t M, int32_t k, void* expert_in, float* expert_scale,
+                      int64_t expert_rows, hipStream_t stream);
+
+/*
+ * moe_combine_partial -- per-(token, bucket) partial sums on the receiver:
+ *
+ *   partial[r] = bf16_rne( sum over j with send_row[t,j] = r, j ascending,
+ *                          of w[t,j] * expert_out[slot[t,j]] )
+ *
+ * fp32 accumulator from +0.0, one rounded multiply and one rounded add per term (no
+ * fused multiply-add), one final rounding -- the order rule of "Purlin: Separating
+ * Orchestration from the Datapath of Collectives", section 3.3 (SCORE).
+ *
+ *   expert_out  bf16 [expert_rows, N], slot-indexed, 16-byte aligned.
+ *   weights     float [M*k]; slot, send_row int32 [M*k] (dedup layout).
+ *   partial     bf16 [partial_rows, N]; rows named by send_row are written.
+ * Entries with a slot outside [0, expert_rows) contribute nothing; send rows outside
+ * [0, partial_rows) are skipped.
+ * Errors: as moe_combine.
+ */
+moe_status moe_combine_partial(const uint16_t* expert_out, int64_t expert_rows,
+                               const float* weights, const int32_t* slot,
+                               const int32_t* send_row, int64_t M, int32_t k, int32_t N,
+                               uint16_t* partial, int64_t partial_rows, hipStream_t stream);
+
+/*
+ * moe_combine_reduce -- the sender adds a token's partials:
+ *
+ *   y[t] = bf16_rne( sum over the distinct r in send_row[t, 0..k), ascending (that is,
+ *                    ascending bucket), of f32(partial[r]) )
+ *
+ * fp32 accumulator from +0.0, one final rounding.
+ *   partial  bf16 [partial_rows, N]; send_row int32 [M*k]; y bf16 [M, N].
+ * Errors: as moe_combine.
+ */
+moe_status moe_combine_reduce(const uint16_t* partial, int64_t partial_rows,
+                              const int32_t* send_row, int64_t M, int32_t k, int32_t N,
+                              uint16_t* y, hipStream_t stream);
 
 #ifdef __cplusplus
 }

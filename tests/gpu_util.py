@@ -71,7 +71,7 @@ def gpu_dispatch(w, lay, sentinel=True):
     if xs is not None:
         out_scale = torch.full((cap, xs.shape[1]), float("nan"), dtype=torch.float32,
                                device="cuda")
-    moedl.moe_dispatch(x, lay.send_row, cap, xs, out=out, out_scale=out_scale)
+    moedl.moe_dispatch(x, lay.send_row, cap, xs, out=out, out_scale=out_scale, dedup=lay.dedup)
     return out, out_scale
 
 

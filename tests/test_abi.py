@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(header, loader):
 
 def test_version_and_strings():
     lib = moedl.load()
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == 2
     assert lib.moe_status_string(0) == b"ok"
     assert lib.moe_status_string(3) == b"workspace too small"
 
@@ -77,13 +77,14 @@ def test_layout_argument_errors(kw, status):
     assert layout_call(**kw) == status
 
 
-def dispatch_call(x=P, dtype=0, M=64, N=7168, xs=None, sr=P, k=8, out=P, os_=None, rows=512):
-    return moedl.load().moe_dispatch(x, dtype, M, N, xs, sr, k, out, os_, rows, None)
+def dispatch_call(x=P, dtype=0, M=64, N=7168, xs=None, sr=P, k=8, dd=0, out=P, os_=None, rows=512):
+    return moedl.load().moe_dispatch(x, dtype, M, N, xs, sr, k, dd, out, os_, rows, None)
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(M=-1), INVALID), (dict(N=0), INVALID), (dict(k=0), INVALID), (dict(rows=-1), INVALID),
     (dict(dtype=7), INVALID), (dict(x=None), INVALID), (dict(sr=None), INVALID),
+    (dict(dd=2), INVALID),
     (dict(out=None), INVALID), (dict(x=P + 8), INVALID), (dict(out=P + 2), INVALID),
     (dict(xs=P), INVALID),                          # scales without out_scale
     (dict(xs=P, os_=P), INVALID),                   # scales with bf16
@@ -115,3 +116,46 @@ def test_harness_argument_errors():
     assert lib.moe_harness_copy(P + 4, P, 16, None) == 1
     assert lib.moe_harness_copy(P, P, 0, None) == 0
     assert lib.moe_harness_expert_outputs(5, P, None, 1, 128, P, P, P, 1, 1, P, 1, None) == 1
+
+
+def expand_call(recv=P, dtype=0, R=512, N=7168, rs=None, sr=P, sl=P, M=64, k=8, ein=P, es=None,
+                rows=512):
+    return moedl.load().moe_expand(recv, dtype, R, N, rs, sr, sl, M, k, ein, es, rows, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=-1), INVALID), (dict(N=0), INVALID), (dict(k=0), INVALID), (dict(R=-1), INVALID),
+    (dict(rows=-1), INVALID), (dict(dtype=3), INVALID), (dict(recv=None), INVALID),
+    (dict(sr=None), INVALID), (dict(sl=None), INVALID), (dict(ein=None), INVALID),
+    (dict(recv=P + 4), INVALID), (dict(rs=P), INVALID), (dict(rs=P, es=P), INVALID),
+    (dict(k=17), UNSUPPORTED), (dict(N=7164), UNSUPPORTED),
+    (dict(dtype=1, N=7184, rs=P, es=P), UNSUPPORTED),
+])
+def test_expand_argument_errors(kw, status):
+    assert expand_call(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=-1), INVALID), (dict(k=0), INVALID), (dict(rows=-1), INVALID), (dict(prow=-1), INVALID),
+    (dict(w=None), INVALID), (dict(sr=None), INVALID), (dict(part=None), INVALID),
+    (dict(eo=P + 2), INVALID), (dict(k=17), UNSUPPORTED), (dict(N=100), UNSUPPORTED),
+])
+def test_combine_partial_argument_errors(kw, status):
+    a = dict(eo=P, rows=512, w=P, slot=P, sr=P, M=64, k=8, N=7168, part=P, prow=512)
+    a.update(kw)
+    lib = moedl.load()
+    assert lib.moe_combine_partial(a["eo"], a["rows"], a["w"], a["slot"], a["sr"], a["M"], a["k"],
+                                   a["N"], a["part"], a["prow"], None) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=-1), INVALID), (dict(k=0), INVALID), (dict(prow=-1), INVALID), (dict(part=None), INVALID),
+    (dict(sr=None), INVALID), (dict(y=None), INVALID), (dict(y=P + 8), INVALID),
+    (dict(k=17), UNSUPPORTED), (dict(N=7164), UNSUPPORTED),
+])
+def test_combine_reduce_argument_errors(kw, status):
+    a = dict(part=P, prow=512, sr=P, M=64, k=8, N=7168, y=P)
+    a.update(kw)
+    lib = moedl.load()
+    assert lib.moe_combine_reduce(a["part"], a["prow"], a["sr"], a["M"], a["k"], a["N"], a["y"],
+                                  None) == status
