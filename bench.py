@@ -18,6 +18,7 @@ oracle timed on the same inputs.
     python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--dedup] [--no-cpu]
     python bench.py --path bucket    # dedup round trip: layout, dispatch, moe_expand,
                                      # moe_combine_partial, moe_combine_reduce
+    python bench.py --path placement --cfg 4   # pair counts, greedy placement, savings
 """
 from __future__ import annotations
 
@@ -51,8 +52,9 @@ def parse():
     ap.add_argument("--dedup", action="store_true", help="time dedup mode instead")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay leg")
-    ap.add_argument("--path", choices=["flat", "bucket"], default="flat",
-                    help="flat: layout+dispatch+combine; bucket: the dedup round trip")
+    ap.add_argument("--path", choices=["flat", "bucket", "placement"], default="flat",
+                    help="flat: layout+dispatch+combine; bucket: the dedup round trip; "
+                         "placement: pair counts + greedy placement and their dedup savings")
     ap.add_argument("--cfg", type=int, default=3, help=argparse.SUPPRESS)
     return ap.parse_args()
 
@@ -176,6 +178,57 @@ def bench_bucket(args, w, dev):
     print(json.dumps(res))
 
 
+def bench_placement(args, w, dev):
+    """Expert pair counts on the GPU, greedy placement on the host, and the send rows
+    a dedup layout needs under round-robin, pair-aware and greedy maps."""
+    import torch
+    from combine_dispatch_layout_amd import moedl, workloads
+    M, G, k, B = w.M, w.G, w.k, w.B
+    idx = torch.from_numpy(w.topk_idx).to(dev)
+    C = moedl.moe_expert_pair_counts(idx, G)
+    for _ in range(max(1, args.warmup)):
+        moedl.moe_expert_pair_counts(idx, G, out=C)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(args.steps):
+        moedl.moe_expert_pair_counts(idx, G, out=C)
+    e.record()
+    torch.cuda.synchronize()
+    counts_us = s.elapsed_time(e) * 1e3 / args.steps
+    t0 = time.perf_counter()
+    greedy = moedl.moe_place_experts(C, B)
+    greedy_ms = (time.perf_counter() - t0) * 1e3
+    maps = {"round_robin": workloads.round_robin_buckets(G, B), "greedy": greedy}
+    if "hot_pairs" in w.meta:
+        maps["pair_aware"] = workloads.pair_aware_buckets(w.meta["hot_pairs"], G, B)
+    if G % B == 0:
+        maps["contiguous"] = workloads.contiguous_buckets(G, B)
+    rows = {}
+    for name, m in maps.items():
+        lay = moedl.moe_dispatch_layout(idx, torch.from_numpy(m).to(dev), B, True)
+        torch.cuda.synchronize()
+        rows[name] = int(lay.bucket_offset[B].item())
+    saving = {n: round(1 - r / (M * k), 4) for n, r in rows.items()}
+    # out of sample: place from the first half of the tokens, measure on the second
+    h = M // 2
+    Ch = moedl.moe_expert_pair_counts(idx[:h].contiguous(), G)
+    holdout_map = moedl.moe_place_experts(Ch, B)
+    holdout = {}
+    for name, m in (("greedy_from_first_half", holdout_map), ("round_robin", maps["round_robin"])) + \
+            ((("pair_aware", maps["pair_aware"]),) if "pair_aware" in maps else ()):
+        lay = moedl.moe_dispatch_layout(idx[h:].contiguous(), torch.from_numpy(m).to(dev), B, True)
+        torch.cuda.synchronize()
+        holdout[name] = round(1 - int(lay.bucket_offset[B].item()) / ((M - h) * k), 4)
+    res = {"metric": "expert placement: dedup saving (fraction of token copies removed)",
+           "value": saving["greedy"], "unit": "fraction", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "higher_is_better": True, "vs_baseline": None,
+           "data": "synthetic", "config": {"workload": w.name, "M": M, "G": G, "k": k, "B": B},
+           "send_rows": rows, "dedup_saving": saving, "dedup_saving_second_half": holdout,
+           "pair_counts_us": round(counts_us, 2), "greedy_host_ms": round(greedy_ms, 3)}
+    print(json.dumps(res))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -195,6 +248,9 @@ def main():
     w = workloads.make_workload(args.cfg)
     if args.path == "bucket":
         bench_bucket(args, w, dev)
+        return
+    if args.path == "placement":
+        bench_placement(args, w, dev)
         return
     M, N, G, k, B = w.M, w.N, w.G, w.k, w.B
     row_bytes = w.row_bytes

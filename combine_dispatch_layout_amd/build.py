@@ -32,7 +32,8 @@ COMMON = [
 ]
 
 LIBS = {
-    "libmoedl.so": ["api.cpp", "layout.hip", "dispatch.hip", "combine.hip", "bucket.hip"],
+    "libmoedl.so": ["api.cpp", "layout.hip", "dispatch.hip", "combine.hip", "bucket.hip",
+                    "placement.hip"],
     "libmoedl_harness.so": ["harness.hip"],
 }
 

@@ -149,4 +149,22 @@ moe_status moe_combine_reduce(const uint16_t* partial, int64_t partial_rows,
       moedl::launch_combine_reduce(partial, partial_rows, send_row, M, k, N, y, stream));
 }
 
+moe_status moe_expert_pair_counts(const int32_t* topk_idx, int64_t M, int32_t k, int32_t G,
+                                  int32_t* pair_counts, hipStream_t stream) {
+  if (M < 0 || k < 1 || G < 1 || !pair_counts) return MOE_ERR_INVALID_ARGUMENT;
+  if (G > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
+  if (M * (int64_t)k >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+  if (M > 0 && !topk_idx) return MOE_ERR_INVALID_ARGUMENT;
+  return from_hip(moedl::launch_pair_counts(topk_idx, M, k, G, pair_counts, stream));
+}
+
+moe_status moe_place_experts(const int32_t* pair_counts, int32_t G, int32_t B,
+                             int32_t* expert_bucket) {
+  if (!pair_counts || !expert_bucket || G < 1 || B < 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (G > MOE_MAX_EXPERTS || B > MOE_MAX_BUCKETS) return MOE_ERR_UNSUPPORTED;
+  if (G % B != 0) return MOE_ERR_INVALID_ARGUMENT;
+  moedl::place_experts_greedy(pair_counts, G, B, expert_bucket);
+  return MOE_OK;
+}
+
 }  // extern "C"

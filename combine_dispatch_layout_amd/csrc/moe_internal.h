@@ -60,6 +60,11 @@ hipError_t launch_combine_reduce(const uint16_t* partial, int64_t partial_rows,
                                  const int32_t* send_row, int64_t M, int32_t k, int32_t N,
                                  uint16_t* y, hipStream_t stream);
 
+hipError_t launch_pair_counts(const int32_t* topk_idx, int64_t M, int32_t k, int32_t G,
+                              int32_t* counts, hipStream_t stream);
+
+void place_experts_greedy(const int32_t* pair_counts, int32_t G, int32_t B, int32_t* bucket);
+
 // ---------------------------------------------------------------- device helpers
 #if defined(__HIP_DEVICE_COMPILE__) || defined(__HIPCC__)
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

@@ -49,6 +49,8 @@ SIGNATURES = {
     "moe_combine_partial": (ctypes.c_int, [
         _vp, _i64, _vp, _i32p, _i32p, _i64, _i32, _i32, _vp, _i64, _vp]),
     "moe_combine_reduce": (ctypes.c_int, [_vp, _i64, _i32p, _i64, _i32, _i32, _vp, _vp]),
+    "moe_expert_pair_counts": (ctypes.c_int, [_i32p, _i64, _i32, _i32, _i32p, _vp]),
+    "moe_place_experts": (ctypes.c_int, [_vp, _i32, _i32, _vp]),
 }
 
 
@@ -242,3 +244,27 @@ def moe_combine_reduce(partial: torch.Tensor, send_row: torch.Tensor,
                                   _stream(stream))
     _check("moe_combine_reduce", st)
     return y
+
+
+def moe_expert_pair_counts(topk_idx: torch.Tensor, G: int, out: Optional[torch.Tensor] = None,
+                           stream=None) -> torch.Tensor:
+    """Expert pair co-occurrence counts, int32 [G, G] on the device."""
+    M, k = topk_idx.shape
+    if out is None:
+        out = torch.empty((G, G), dtype=torch.int32, device=topk_idx.device)
+    st = lib().moe_expert_pair_counts(_ptr(topk_idx), M, k, G, _ptr(out), _stream(stream))
+    _check("moe_expert_pair_counts", st)
+    return out
+
+
+def moe_place_experts(pair_counts, B: int):
+    """Greedy expert -> bucket placement on the host.  pair_counts: int32 [G, G]
+    (numpy array or tensor, copied to host).  Returns a numpy int32 [G] map."""
+    import numpy as np
+    C = pair_counts.cpu().numpy() if isinstance(pair_counts, torch.Tensor) else pair_counts
+    C = np.ascontiguousarray(C, dtype=np.int32)
+    G = C.shape[0]
+    out = np.empty(G, dtype=np.int32)
+    st = lib().moe_place_experts(C.ctypes.data, G, B, out.ctypes.data)
+    _check("moe_place_experts", st)
+    return out

@@ -7,9 +7,10 @@ pair statistics item: a few expert pairs carry a large share of tokens).  The pa
 gives the idea, not an algorithm.  What is built here, and its reading:
 
 * pair_counts: C[a, b] = number of tokens whose expert set contains both a and b
-  (a token's repeated expert counts once); the diagonal C[a, a] is the number of
-  tokens that choose a.  With S the 0/1 token-by-expert incidence matrix this is
-  exactly C = S^T S, which is how it is computed here.
+  (a token's repeated expert counts once; ids outside [0, G) are left out); the
+  diagonal C[a, a] is the number of tokens that choose a.  With S the 0/1
+  token-by-expert incidence matrix this is exactly C = S^T S, which is how it is
+  computed here.
 * greedy_place(C, B): every bucket holds G/B experts.  Steps, in order:
     1. every expert starts as its own cluster;
     2. the pairs (a < b) with C[a, b] > 0 are visited by count descending, ties by
@@ -31,7 +32,10 @@ def pair_counts(topk_idx: np.ndarray, G: int) -> np.ndarray:
     idx = np.asarray(topk_idx, dtype=np.int64)
     M = idx.shape[0]
     S = np.zeros((M, G), dtype=np.int64)
-    S[np.repeat(np.arange(M), idx.shape[1]), idx.reshape(-1)] = 1
+    tok = np.repeat(np.arange(M), idx.shape[1])
+    e = idx.reshape(-1)
+    ok = (e >= 0) & (e < G)
+    S[tok[ok], e[ok]] = 1
     return S.T @ S
 
 

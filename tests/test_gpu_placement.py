@@ -1,0 +1,47 @@
+"""GPU parity of the expert pair co-occurrence counts, and the placement chain
+(counts on the GPU -> host greedy -> dedup layout on the GPU) against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from combine_dispatch_layout_amd import moedl
+from combine_dispatch_layout_amd import workloads as wl
+from gpu_util import dev, host, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_pair_counts_full_size(gpu_lib, cfg):
+    w = wl.make_workload(cfg, with_rows=False)
+    say(f"pair counts {w.name}")
+    got = host(moedl.moe_expert_pair_counts(dev(w.topk_idx), w.G))
+    assert np.array_equal(got, oracle.pair_counts(w.topk_idx, w.G))
+
+
+@pytest.mark.parametrize("M,k,G,routing,seed", [(0, 8, 64, "uniform", 0), (1, 8, 256, "uniform", 1),
+                                                (777, 5, 37, "repeats", 2), (300, 16, 1024, "uniform", 3),
+                                                (513, 1, 8, "uniform", 4), (400, 4, 16, "one_expert", 5)])
+def test_pair_counts_edges(gpu_lib, M, k, G, routing, seed):
+    if M == 0:
+        idx = np.zeros((0, k), dtype=np.int32)
+    else:
+        idx = wl.make_custom(M, 16, G, k, 1, routing=routing, seed=seed).topk_idx.copy()
+        idx[::7, 0] = -3                                     # ids outside [0, G) are ignored
+        idx[::11, -1] = G + 5
+    got = host(moedl.moe_expert_pair_counts(dev(idx), G))
+    assert np.array_equal(got, oracle.pair_counts(idx, G))
+
+
+def test_placement_chain(gpu_lib):
+    w = wl.make_workload(4, with_rows=False)
+    C = moedl.moe_expert_pair_counts(dev(w.topk_idx), w.G)
+    m = moedl.moe_place_experts(C, w.B)
+    assert np.array_equal(m, oracle.greedy_place(oracle.pair_counts(w.topk_idx, w.G), w.B))
+    lay = moedl.moe_dispatch_layout(dev(w.topk_idx), dev(m), w.B, True)
+    torch.cuda.synchronize()
+    ref = oracle.dispatch_layout(w.topk_idx, m, w.B, True)
+    assert int(lay.bucket_offset[w.B].item()) == ref.R
+    rr = oracle.dispatch_layout(w.topk_idx, wl.round_robin_buckets(w.G, w.B), w.B, True).R
+    assert ref.R < rr

@@ -24,7 +24,7 @@ from oracle.placement import greedy_clusters, greedy_place, pair_counts
 def test_pair_counts_brute_force(seed):
     rng = np.random.default_rng(seed)
     M, k, G = int(rng.integers(1, 40)), int(rng.integers(1, 6)), int(rng.integers(2, 12))
-    idx = rng.integers(0, G, size=(M, k))
+    idx = rng.integers(-1, G + 1, size=(M, k))      # repeats and out-of-range ids
     C = pair_counts(idx, G)
     for a, b in itertools.product(range(G), repeat=2):
         want = sum(1 for t in range(M) if a in set(idx[t]) and b in set(idx[t]))
