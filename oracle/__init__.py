@@ -27,7 +27,8 @@ Modules: ``numerics`` (bf16 / fp8 e4m3 codecs), ``layout`` (counts, offsets, slo
 map, dedup rows), ``dispatch`` (row scatter), ``combine`` (weighted top-k sum),
 ``bucket_combine`` (receiver-side expansion of dedup rows, per-(token, bucket)
 pre-reduced combine), ``placement`` (expert pair co-occurrence counts and the greedy
-correlation-aware expert -> bucket placement), ``standins`` (expert stand-ins used between dispatch and
+correlation-aware expert -> bucket placement), ``grouped_gemm`` (the expert GEMM over
+the per-expert layout and its tile metadata), ``standins`` (expert stand-ins used between dispatch and
 combine in tests).
 
 Parity pins: every function here is pinned in ``tests/test_oracle_*.py`` against
@@ -41,10 +42,11 @@ from .combine import combine
 from .standins import expert_outputs
 from .bucket_combine import expand, combine_partial, combine_reduce
 from .placement import pair_counts, greedy_clusters, greedy_place
+from .grouped_gemm import gemm_tiles, grouped_gemm
 
 __all__ = [
     "bf16_to_f32", "f32_to_bf16_rne", "e4m3_to_f32", "f32_to_e4m3_rne_sat",
     "Layout", "dispatch_layout", "dispatch_layout_loops", "dispatch", "combine",
     "expert_outputs", "expand", "combine_partial", "combine_reduce",
-    "pair_counts", "greedy_clusters", "greedy_place",
+    "pair_counts", "greedy_clusters", "greedy_place", "gemm_tiles", "grouped_gemm",
 ]
