@@ -19,6 +19,7 @@ oracle timed on the same inputs.
     python bench.py --path bucket    # dedup round trip: layout, dispatch, moe_expand,
                                      # moe_combine_partial, moe_combine_reduce
     python bench.py --path placement --cfg 4   # pair counts, greedy placement, savings
+    python bench.py --path gemm      # tile metadata + MFMA grouped GEMM over the layout
 """
 from __future__ import annotations
 
@@ -52,9 +53,11 @@ def parse():
     ap.add_argument("--dedup", action="store_true", help="time dedup mode instead")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay leg")
-    ap.add_argument("--path", choices=["flat", "bucket", "placement"], default="flat",
+    ap.add_argument("--path", choices=["flat", "bucket", "placement", "gemm"], default="flat",
                     help="flat: layout+dispatch+combine; bucket: the dedup round trip; "
-                         "placement: pair counts + greedy placement and their dedup savings")
+                         "placement: pair counts + greedy placement and their dedup savings; "
+                         "gemm: grouped-GEMM tile metadata + the MFMA grouped GEMM")
+    ap.add_argument("--nout", type=int, default=2048, help="grouped GEMM output width")
     ap.add_argument("--cfg", type=int, default=3, help=argparse.SUPPRESS)
     return ap.parse_args()
 
@@ -229,6 +232,97 @@ def bench_placement(args, w, dev):
     print(json.dumps(res))
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def _time_gemm(moedl, torch, x, wt, tiles, y, lay_offset, lay_count, steps, warmup):
+    """Mean event time (us) of moe_grouped_gemm_tiles and moe_grouped_gemm over `steps`."""
+    rows = x.shape[0]
+    calls = [lambda: moedl.moe_grouped_gemm_tiles(lay_offset, lay_count, rows, out=tiles),
+             lambda: moedl.moe_grouped_gemm(x, wt, tiles, y=y)]
+    for _ in range(max(1, warmup)):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(stream)
+        for c, e in zip(calls, ev[i][1:]):
+            c()
+            e.record(stream)
+    torch.cuda.synchronize()
+    return [float(np.mean([e[q].elapsed_time(e[q + 1]) for e in ev])) * 1e3 for q in range(2)]
+
+
+def bench_gemm(args, w, dev):
+    """The expert step over the headline layout: every dispatched row (M*k of them,
+    slot-indexed by expert) times its expert's [Nout, N] bf16 weights, fp32 accumulate.
+    Also the grouped-GEMM shape the DeepSpeed page measures (16 experts, 760 tokens,
+    dim 2048 -> hidden 768, unbalanced), as context."""
+    import torch
+    from combine_dispatch_layout_amd import moedl
+    M, N, G, k, B = w.M, w.N, w.G, w.k, w.B
+    Nout = args.nout
+    idx = torch.from_numpy(w.topk_idx).to(dev)
+    ebkt = torch.from_numpy(w.expert_bucket).to(dev)
+    x = torch.from_numpy(w.x.view(np.int16)).to(dev)
+    lay = moedl.alloc_layout(M, k, G, B, False, dev)
+    moedl.moe_dispatch_layout(idx, ebkt, B, False, out=lay)
+    xe = torch.empty((M * k, N), dtype=torch.int16, device=dev)
+    moedl.moe_dispatch(x, lay.send_row, M * k, out=xe)
+    gen = torch.Generator(device=dev).manual_seed(11)
+    wt = (torch.randn((G, Nout, N), generator=gen, device=dev) * 0.02).to(
+        torch.bfloat16).view(torch.int16)
+    tiles = moedl.moe_grouped_gemm_tiles(lay.expert_offset, lay.expert_count, M * k)
+    y = torch.empty((M * k, Nout), dtype=torch.int16, device=dev)
+    t_tiles, t_gemm = _time_gemm(moedl, torch, xe, wt, tiles, y, lay.expert_offset,
+                                 lay.expert_count, args.steps, args.warmup)
+    torch.cuda.synchronize()
+    flops = 2.0 * M * k * N * Nout
+    tflops = flops / (t_gemm * 1e-6) / 1e12
+    # sanity: one sampled row per 4096 against a float32 product on the GPU
+    off_h, cnt_h = lay.expert_offset.cpu().numpy(), lay.expert_count.cpu().numpy()
+    owner = np.full(M * k, -1, dtype=np.int64)
+    for e in range(G):
+        owner[off_h[e]:off_h[e] + cnt_h[e]] = e
+    r = np.arange(0, M * k, 4096)
+    rd, ed = torch.from_numpy(r).to(dev), torch.from_numpy(owner[r]).to(dev)
+    ref = torch.bmm(wt[ed].view(torch.bfloat16).float().contiguous(),
+                    xe[rd].view(torch.bfloat16).float().unsqueeze(2).contiguous()).squeeze(2)
+    got = y[rd].view(torch.bfloat16).float()
+    assert bool(((got - ref).abs() <= ref.abs() * 2.0 ** -7 + 1e-2).all().item()), "gemm check"
+
+    # the DeepSpeed page's grouped-GEMM shape: 16 experts, 760 tokens, 2048 -> 768
+    Gs, Ms, Ks, Ns = 16, 760, 2048, 768
+    rng = np.random.default_rng(12)
+    cnt = rng.multinomial(Ms, rng.dirichlet(np.ones(Gs))).astype(np.int32)
+    off = np.concatenate([[0], np.cumsum(cnt)[:-1]]).astype(np.int32)
+    xs = (torch.randn((Ms, Ks), generator=gen, device=dev)).to(torch.bfloat16).view(torch.int16)
+    ws = (torch.randn((Gs, Ns, Ks), generator=gen, device=dev) * 0.02).to(
+        torch.bfloat16).view(torch.int16)
+    offd, cntd = torch.from_numpy(off).to(dev), torch.from_numpy(cnt).to(dev)
+    ts = moedl.moe_grouped_gemm_tiles(offd, cntd, Ms)
+    ys = torch.empty((Ms, Ns), dtype=torch.int16, device=dev)
+    s_tiles, s_gemm = _time_gemm(moedl, torch, xs, ws, ts, ys, offd, cntd, args.steps, args.warmup)
+
+    res = {"metric": "grouped GEMM TFLOP/s over the per-expert layout (bf16 in/out, fp32 acc)",
+           "value": round(tflops, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round((t_tiles + t_gemm) * 1e-3, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic",
+           "config": {"workload": w.name + "-grouped-gemm", "rows": M * k, "K": N, "Nout": Nout,
+                      "G": G},
+           "roofline": {"bound": "mfma", "achieved": round(tflops, 1),
+                        "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
+           "event_us": {"grouped_gemm_tiles": round(t_tiles, 2), "grouped_gemm": round(t_gemm, 2)},
+           "deepspeed_page_shape": {"experts": Gs, "tokens": Ms, "K": Ks, "Nout": Ns,
+                                    "tiles_us": round(s_tiles, 2), "gemm_us": round(s_gemm, 2),
+                                    "tflops": round(2.0 * Ms * Ks * Ns / (s_gemm * 1e-6) / 1e12, 2)}}
+    print(json.dumps(res))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -251,6 +345,9 @@ def main():
         return
     if args.path == "placement":
         bench_placement(args, w, dev)
+        return
+    if args.path == "gemm":
+        bench_gemm(args, w, dev)
         return
     M, N, G, k, B = w.M, w.N, w.G, w.k, w.B
     row_bytes = w.row_bytes

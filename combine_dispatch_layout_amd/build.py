@@ -33,7 +33,7 @@ COMMON = [
 
 LIBS = {
     "libmoedl.so": ["api.cpp", "layout.hip", "dispatch.hip", "combine.hip", "bucket.hip",
-                    "placement.hip"],
+                    "placement.hip", "gemm.hip"],
     "libmoedl_harness.so": ["harness.hip"],
 }
 

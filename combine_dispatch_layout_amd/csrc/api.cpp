@@ -167,4 +167,37 @@ moe_status moe_place_experts(const int32_t* pair_counts, int32_t G, int32_t B,
   return MOE_OK;
 }
 
+int32_t moe_grouped_gemm_max_tiles(int64_t rows, int32_t G, int32_t tile_m) {
+  if (rows < 0 || G < 1 || tile_m < 1) return 0;
+  const int64_t t = (rows + tile_m - 1) / tile_m + G;
+  return t > 0x7FFFFFFF ? 0x7FFFFFFF : (int32_t)t;
+}
+
+moe_status moe_grouped_gemm_tiles(const int32_t* expert_offset, const int32_t* expert_count,
+                                  int32_t G, int32_t tile_m, int32_t* tile_expert,
+                                  int32_t* tile_row0, int32_t* tile_rows, int32_t max_tiles,
+                                  int32_t* num_tiles, hipStream_t stream) {
+  if (!expert_offset || !expert_count || !num_tiles || G < 1 || tile_m < 1 || max_tiles < 0)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (max_tiles > 0 && (!tile_expert || !tile_row0 || !tile_rows)) return MOE_ERR_INVALID_ARGUMENT;
+  if (G > MOE_MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
+  return from_hip(moedl::launch_gemm_tiles(expert_offset, expert_count, G, tile_m, tile_expert,
+                                           tile_row0, tile_rows, max_tiles, num_tiles, stream));
+}
+
+moe_status moe_grouped_gemm(const uint16_t* x, int64_t rows, int32_t K, const uint16_t* w,
+                            int32_t G, int32_t Nout, const int32_t* tile_expert,
+                            const int32_t* tile_row0, const int32_t* tile_rows,
+                            int32_t max_tiles, uint16_t* y, hipStream_t stream) {
+  if (rows < 0 || K < 1 || G < 1 || Nout < 1 || max_tiles < 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (K % 64 != 0 || Nout % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)max_tiles * (Nout / 128) > (int64_t)1 << 23) return MOE_ERR_UNSUPPORTED;
+  if (!w || (max_tiles > 0 && (!tile_expert || !tile_row0 || !tile_rows))) return MOE_ERR_INVALID_ARGUMENT;
+  if (rows > 0 && (!x || !y)) return MOE_ERR_INVALID_ARGUMENT;
+  if ((x && !aligned16(x)) || !aligned16(w)) return MOE_ERR_INVALID_ARGUMENT;
+  if (rows == 0) return MOE_OK;
+  return from_hip(moedl::launch_grouped_gemm(x, w, K, Nout, tile_expert, tile_row0, tile_rows,
+                                             max_tiles, y, stream));
+}
+
 }  // extern "C"

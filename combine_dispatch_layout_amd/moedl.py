@@ -51,7 +51,14 @@ SIGNATURES = {
     "moe_combine_reduce": (ctypes.c_int, [_vp, _i64, _i32p, _i64, _i32, _i32, _vp, _vp]),
     "moe_expert_pair_counts": (ctypes.c_int, [_i32p, _i64, _i32, _i32, _i32p, _vp]),
     "moe_place_experts": (ctypes.c_int, [_vp, _i32, _i32, _vp]),
+    "moe_grouped_gemm_max_tiles": (ctypes.c_int32, [_i64, _i32, _i32]),
+    "moe_grouped_gemm_tiles": (ctypes.c_int, [
+        _i32p, _i32p, _i32, _i32, _i32p, _i32p, _i32p, _i32, _i32p, _vp]),
+    "moe_grouped_gemm": (ctypes.c_int, [
+        _vp, _i64, _i32, _vp, _i32, _i32, _i32p, _i32p, _i32p, _i32, _vp, _vp]),
 }
+
+GEMM_TILE_M = 128
 
 
 class MoeError(RuntimeError):
@@ -268,3 +275,46 @@ def moe_place_experts(pair_counts, B: int):
     st = lib().moe_place_experts(C.ctypes.data, G, B, out.ctypes.data)
     _check("moe_place_experts", st)
     return out
+
+
+@dataclass
+class GemmTiles:
+    expert: torch.Tensor     # int32 [max_tiles], -1 past the last tile
+    row0: torch.Tensor       # int32 [max_tiles]
+    rows: torch.Tensor       # int32 [max_tiles]
+    num_tiles: torch.Tensor  # int32 [1]
+
+    @property
+    def max_tiles(self) -> int:
+        return self.expert.numel()
+
+
+def moe_grouped_gemm_tiles(expert_offset: torch.Tensor, expert_count: torch.Tensor, rows: int,
+                           tile_m: int = GEMM_TILE_M, out: Optional[GemmTiles] = None,
+                           stream=None) -> GemmTiles:
+    """Row tiles of each expert's run, built on the device (no host sync)."""
+    G = expert_count.numel()
+    if out is None:
+        mt = int(lib().moe_grouped_gemm_max_tiles(rows, G, tile_m))
+        i32 = dict(dtype=torch.int32, device=expert_count.device)
+        out = GemmTiles(torch.empty(mt, **i32), torch.empty(mt, **i32), torch.empty(mt, **i32),
+                        torch.empty(1, **i32))
+    st = lib().moe_grouped_gemm_tiles(_ptr(expert_offset), _ptr(expert_count), G, tile_m,
+                                      _ptr(out.expert), _ptr(out.row0), _ptr(out.rows),
+                                      out.max_tiles, _ptr(out.num_tiles), _stream(stream))
+    _check("moe_grouped_gemm_tiles", st)
+    return out
+
+
+def moe_grouped_gemm(x: torch.Tensor, w: torch.Tensor, tiles: GemmTiles,
+                     y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """y = per-expert x @ w[e].T (bf16 bits in and out, fp32 accumulation)."""
+    rows, K = x.shape
+    G, Nout, _ = w.shape
+    if y is None:
+        y = torch.empty((rows, Nout), dtype=x.dtype, device=x.device)
+    st = lib().moe_grouped_gemm(_ptr(x), rows, K, _ptr(w), G, Nout, _ptr(tiles.expert),
+                                _ptr(tiles.row0), _ptr(tiles.rows), tiles.max_tiles, _ptr(y),
+                                _stream(stream))
+    _check("moe_grouped_gemm", st)
+    return y

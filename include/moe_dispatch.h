@@ -286,6 +286,52 @@ moe_status moe_expert_pair_counts(const int32_t* topk_idx, int64_t M, int32_t k,
 moe_status moe_place_experts(const int32_t* pair_counts, int32_t G, int32_t B,
                              int32_t* expert_bucket);
 
+/*
+ * ---------------------------------------------------------------------------------
+ * The expert step between dispatch and combine: a grouped GEMM over the per-expert
+ * layout, driven by tile metadata built on the device from the layout's offsets, with
+ * no device -> host synchronisation ("Add Triton grouped-GEMM for MoE experts on
+ * Ampere/Ada", "What this PR does": 2D x 3D with per-group offsets, a tile -> group
+ * map computed on the device, weights in their native [E, N, K] layout).
+ * ---------------------------------------------------------------------------------
+ */
+#define MOE_GEMM_TILE_M 128 /* rows per tile moe_grouped_gemm expects */
+
+/* Host-side bound on the number of row tiles: ceil(rows / tile_m) + G. */
+int32_t moe_grouped_gemm_max_tiles(int64_t rows, int32_t G, int32_t tile_m);
+
+/*
+ * moe_grouped_gemm_tiles -- row tiles of each expert's run (device):
+ *   experts in ascending id; expert e's rows [expert_offset[e], +expert_count[e]) cut
+ *   into tiles of tile_m rows (the last shorter).  For t < num_tiles:
+ *   tile_expert[t] = e, tile_row0[t] = first row, tile_rows[t] = rows; entries
+ *   t >= num_tiles (up to max_tiles) get tile_expert = -1.
+ *   expert_offset, expert_count  int32 [G] from moe_dispatch_layout.
+ *   tile_expert, tile_row0, tile_rows  int32 [max_tiles]; num_tiles int32 [1].
+ * Errors: MOE_ERR_INVALID_ARGUMENT (null, G < 1, tile_m < 1, max_tiles < 0),
+ * MOE_ERR_UNSUPPORTED (G > 1024), MOE_ERR_LAUNCH.
+ */
+moe_status moe_grouped_gemm_tiles(const int32_t* expert_offset, const int32_t* expert_count,
+                                  int32_t G, int32_t tile_m, int32_t* tile_expert,
+                                  int32_t* tile_row0, int32_t* tile_rows, int32_t max_tiles,
+                                  int32_t* num_tiles, hipStream_t stream);
+
+/*
+ * moe_grouped_gemm -- y[r, n] = bf16_rne( sum_k x[r, k] * w[e, n, k] ) for every row r
+ * of a tile of expert e, fp32 accumulation on the matrix cores
+ * (v_mfma_f32_32x32x16_bf16).
+ *   x  bf16 [rows, K] (slot-indexed expert inputs), w bf16 [G, Nout, K],
+ *   tiles from moe_grouped_gemm_tiles with tile_m = MOE_GEMM_TILE_M,
+ *   y  bf16 [rows, Nout]; rows outside every tile are not written.
+ * Errors: MOE_ERR_INVALID_ARGUMENT (null or misaligned pointers, sizes < 1),
+ * MOE_ERR_UNSUPPORTED (K % 64 != 0, Nout % 128 != 0, max_tiles * Nout / 128 > 2^23),
+ * MOE_ERR_LAUNCH.  The tile arrays are trusted: every tile's rows must lie in [0, rows).
+ */
+moe_status moe_grouped_gemm(const uint16_t* x, int64_t rows, int32_t K, const uint16_t* w,
+                            int32_t G, int32_t Nout, const int32_t* tile_expert,
+                            const int32_t* tile_row0, const int32_t* tile_rows,
+                            int32_t max_tiles, uint16_t* y, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

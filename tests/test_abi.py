@@ -159,3 +159,42 @@ def test_combine_reduce_argument_errors(kw, status):
     lib = moedl.load()
     assert lib.moe_combine_reduce(a["part"], a["prow"], a["sr"], a["M"], a["k"], a["N"], a["y"],
                                   None) == status
+
+
+def test_grouped_gemm_max_tiles():
+    lib = moedl.load()
+    assert lib.moe_grouped_gemm_max_tiles(131072, 256, 128) == 1024 + 256
+    assert lib.moe_grouped_gemm_max_tiles(0, 8, 128) == 8
+    assert lib.moe_grouped_gemm_max_tiles(1, 8, 128) == 9
+    assert lib.moe_grouped_gemm_max_tiles(-1, 8, 128) == 0
+    assert lib.moe_grouped_gemm_max_tiles(10, 0, 128) == 0
+    assert lib.moe_grouped_gemm_max_tiles(10, 8, 0) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(off=None), INVALID), (dict(cnt=None), INVALID), (dict(num=None), INVALID),
+    (dict(G=0), INVALID), (dict(tm=0), INVALID), (dict(mt=-1), INVALID),
+    (dict(te=None), INVALID), (dict(tr=None), INVALID), (dict(tn=None), INVALID),
+    (dict(G=1025), UNSUPPORTED),
+])
+def test_grouped_gemm_tiles_argument_errors(kw, status):
+    a = dict(off=P, cnt=P, G=256, tm=128, te=P, tr=P, tn=P, mt=1280, num=P)
+    a.update(kw)
+    lib = moedl.load()
+    assert lib.moe_grouped_gemm_tiles(a["off"], a["cnt"], a["G"], a["tm"], a["te"], a["tr"],
+                                      a["tn"], a["mt"], a["num"], None) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(rows=-1), INVALID), (dict(K=0), INVALID), (dict(G=0), INVALID), (dict(Nout=0), INVALID),
+    (dict(mt=-1), INVALID), (dict(w=None), INVALID), (dict(te=None), INVALID),
+    (dict(x=None), INVALID), (dict(y=None), INVALID), (dict(x=P + 2), INVALID),
+    (dict(w=P + 8), INVALID), (dict(K=7160), UNSUPPORTED), (dict(Nout=2000), UNSUPPORTED),
+    (dict(mt=1 << 21, Nout=1024), UNSUPPORTED), (dict(rows=0, x=None, y=None), OK),
+])
+def test_grouped_gemm_argument_errors(kw, status):
+    a = dict(x=P, rows=512, K=7168, w=P, G=256, Nout=2048, te=P, tr=P, tn=P, mt=260, y=P)
+    a.update(kw)
+    lib = moedl.load()
+    assert lib.moe_grouped_gemm(a["x"], a["rows"], a["K"], a["w"], a["G"], a["Nout"], a["te"],
+                                a["tr"], a["tn"], a["mt"], a["y"], None) == status

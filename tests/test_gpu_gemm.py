@@ -1,0 +1,133 @@
+"""GPU parity of the grouped-GEMM tile metadata (bit for bit) and of the MFMA grouped
+GEMM against the exact (float64) products of the oracle.
+
+Tolerance, from the arithmetic: the GPU accumulates K products in fp32 (each product of
+two bf16 is exact in fp32; K - 1 rounded adds give |error| < K * 2^-24 * sum|x w| with
+round-to-nearest, K * 2^-23 * sum|x w| even with truncation) and rounds once to bf16
+(|error| <= 2^-8 |value|, half an ulp of an 8-bit significand), so every element must
+satisfy
+    |y - exact| <= 2^-8 |exact| + K * 2^-22 * sum_k |x w|.
+The second assertion keeps the check from being vacuous: almost every element is
+within one bf16 rounding of the exact value.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from combine_dispatch_layout_amd import moedl
+from combine_dispatch_layout_amd import workloads as wl
+from gpu_util import dev, host, say
+from oracle.grouped_gemm import magnitude
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf16(rng, shape, scale=1.0):
+    return oracle.f32_to_bf16_rne((rng.standard_normal(shape) * scale).astype(np.float32))
+
+
+def _check_tiles(lay_gpu, ref, rows):
+    tiles = moedl.moe_grouped_gemm_tiles(lay_gpu.expert_offset, lay_gpu.expert_count, rows)
+    torch.cuda.synchronize()
+    want = oracle.gemm_tiles(ref.expert_offset, ref.expert_count, moedl.GEMM_TILE_M)
+    n = int(tiles.num_tiles.item())
+    assert n == len(want)
+    got = list(zip(host(tiles.expert)[:n].tolist(), host(tiles.row0)[:n].tolist(),
+                   host(tiles.rows)[:n].tolist()))
+    assert got == want
+    assert np.all(host(tiles.expert)[n:] == -1)
+    return tiles
+
+
+def _bound_check(got, exact, mag, K, ctx):
+    err = np.abs(got - exact)
+    bound = 2.0 ** -8 * np.abs(exact) + K * 2.0 ** -22 * mag
+    assert np.all(err <= bound), (ctx, float((err - bound).max()))
+    assert np.mean(err <= 2.0 ** -8 * np.abs(exact)) > 0.99, ctx
+
+
+def _check_gemm(x, w, ref, tiles, ctx=""):
+    """Whole output against the oracle; x, w host bf16 bits."""
+    K = x.shape[1]
+    y = moedl.moe_grouped_gemm(dev(x.view(np.int16)), dev(w.view(np.int16)), tiles)
+    torch.cuda.synchronize()
+    exact = oracle.grouped_gemm(x, w, ref.expert_offset, ref.expert_count)
+    mag = magnitude(x, w, ref.expert_offset, ref.expert_count)
+    got = oracle.bf16_to_f32(host(y).view(np.uint16)).astype(np.float64)
+    _bound_check(got, exact, mag, K, ctx)
+
+
+def _row_owner(ref, rows):
+    owner = np.full(rows, -1, dtype=np.int64)
+    for e in range(len(ref.expert_count)):
+        o, c = int(ref.expert_offset[e]), int(ref.expert_count[e])
+        owner[o:o + c] = e
+    return owner
+
+
+@pytest.mark.parametrize("cfg,M,K,Nout", [(2, 512, 1024, 256), (3, 512, 1024, 256),
+                                          (4, 700, 512, 384)])
+def test_grouped_gemm_reduced(gpu_lib, cfg, M, K, Nout):
+    w_ = wl.make_workload(cfg, M=M, with_rows=False)
+    say(f"grouped gemm {w_.name} M={M} K={K} Nout={Nout}")
+    ref = oracle.dispatch_layout(w_.topk_idx, w_.expert_bucket, w_.B, False)
+    lay = moedl.moe_dispatch_layout(dev(w_.topk_idx), dev(w_.expert_bucket), w_.B, False)
+    rows = w_.M * w_.k
+    tiles = _check_tiles(lay, ref, rows)
+    rng = np.random.default_rng([cfg, M])
+    x = _bf16(rng, (rows, K))
+    w = _bf16(rng, (w_.G, Nout, K), scale=0.05)
+    _check_gemm(x, w, ref, tiles, ctx=w_.name)
+
+
+def test_grouped_gemm_edges(gpu_lib):
+    """Experts with 0, 1, 127, 128, 129 and 300 rows; K = 64, Nout = 128."""
+    counts = [0, 1, 127, 128, 129, 300, 0, 5]
+    G = len(counts)
+    idx = np.concatenate([np.full(c, e, np.int32) for e, c in enumerate(counts)]).reshape(-1, 1)
+    rng = np.random.default_rng(1)
+    idx = idx[rng.permutation(len(idx))]
+    ebkt = np.zeros(G, np.int32)
+    ref = oracle.dispatch_layout(idx, ebkt, 1, False)
+    lay = moedl.moe_dispatch_layout(dev(idx), dev(ebkt), 1, False)
+    rows = len(idx)
+    tiles = _check_tiles(lay, ref, rows)
+    for K, Nout in ((64, 128), (192, 256)):
+        x = _bf16(rng, (rows, K))
+        w = _bf16(rng, (G, Nout, K), scale=0.1)
+        _check_gemm(x, w, ref, tiles, ctx=f"K={K} Nout={Nout}")
+
+
+def test_grouped_gemm_full_size_sampled(gpu_lib):
+    """Zipf M=16384 top-8 (131072 rows, the hottest expert ~15k of them), K=7168,
+    Nout=256: 200 sampled rows plus the first and last, each against the oracle run
+    on that row and its expert's weights."""
+    w_ = wl.make_workload(3, with_rows=False)
+    say("grouped gemm full size, sampled rows")
+    ref = oracle.dispatch_layout(w_.topk_idx, w_.expert_bucket, w_.B, False)
+    lay = moedl.moe_dispatch_layout(dev(w_.topk_idx), dev(w_.expert_bucket), w_.B, False)
+    rows, K, Nout = w_.M * w_.k, 7168, 256
+    tiles = _check_tiles(lay, ref, rows)
+    g = torch.Generator(device="cuda").manual_seed(5)
+    xd = torch.randn((rows, K), generator=g, device="cuda").to(torch.bfloat16).view(torch.int16)
+    wd = (torch.randn((w_.G, Nout, K), generator=g, device="cuda") * 0.02).to(
+        torch.bfloat16).view(torch.int16)
+    y = moedl.moe_grouped_gemm(xd, wd, tiles)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    sample = np.unique(np.concatenate([rng.choice(rows, 200, replace=False), [0, rows - 1]]))
+    owner = _row_owner(ref, rows)[sample]
+    assert np.all(owner >= 0)
+    xs = host(xd[dev(sample)]).view(np.uint16)
+    ws = host(wd[dev(owner)]).view(np.uint16)                     # [s, Nout, K]
+    # each sampled row is a one-row group of its own expert
+    one = np.ones(len(sample), dtype=np.int64)
+    offs = np.arange(len(sample), dtype=np.int64)
+    exact = np.zeros((len(sample), Nout))
+    mag = np.zeros((len(sample), Nout))
+    for i in range(len(sample)):
+        exact[i] = oracle.grouped_gemm(xs[i:i + 1], ws[i:i + 1], offs[:1], one[:1])[0]
+        mag[i] = magnitude(xs[i:i + 1], ws[i:i + 1], offs[:1], one[:1])[0]
+    got = oracle.bf16_to_f32(host(y[dev(sample)]).view(np.uint16)).astype(np.float64)
+    _bound_check(got, exact, mag, K, "full size")
