@@ -20,6 +20,7 @@ oracle timed on the same inputs.
                                      # moe_combine_partial, moe_combine_reduce
     python bench.py --path placement --cfg 4   # pair counts, greedy placement, savings
     python bench.py --path gemm      # tile metadata + MFMA grouped GEMM over the layout
+    python bench.py --path small     # small M: fused layout+dispatch vs separate calls
 """
 from __future__ import annotations
 
@@ -53,10 +54,12 @@ def parse():
     ap.add_argument("--dedup", action="store_true", help="time dedup mode instead")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay leg")
-    ap.add_argument("--path", choices=["flat", "bucket", "placement", "gemm"], default="flat",
+    ap.add_argument("--path", choices=["flat", "bucket", "placement", "gemm", "small"],
+                    default="flat",
                     help="flat: layout+dispatch+combine; bucket: the dedup round trip; "
                          "placement: pair counts + greedy placement and their dedup savings; "
-                         "gemm: grouped-GEMM tile metadata + the MFMA grouped GEMM")
+                         "gemm: grouped-GEMM tile metadata + the MFMA grouped GEMM; "
+                         "small: latency at M <= 512, fused layout+dispatch vs three calls")
     ap.add_argument("--nout", type=int, default=2048, help="grouped GEMM output width")
     ap.add_argument("--cfg", type=int, default=3, help=argparse.SUPPRESS)
     return ap.parse_args()
@@ -323,6 +326,88 @@ def bench_gemm(args, w, dev):
     print(json.dumps(res))
 
 
+def graph_replay_us(torch, step, invocations=128, timed=8):
+    """[PURLIN] section 5 method: `invocations` steps captured in one graph, one warm-up
+    replay, `timed` timed replays; microseconds per step."""
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for _ in range(invocations):
+            step()
+    g.replay()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(timed):
+        g.replay()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) * 1e3 / (invocations * timed)
+
+
+def bench_small(args, dev):
+    """Small batches (N=7168 bf16, G=256, top-8 uniform, 8 contiguous buckets, identity
+    experts): a step is dispatch layout + row scatter + combine, either as three calls
+    or with moe_layout_dispatch doing the first two in one launch."""
+    import torch
+    from combine_dispatch_layout_amd import moedl, workloads
+    rows = []
+    for M in (64, 128, 256, 512):
+        w = workloads.make_workload(1, M=M)
+        N, G, k, B = w.N, w.G, w.k, w.B
+        idx = torch.from_numpy(w.topk_idx).to(dev)
+        ebkt = torch.from_numpy(w.expert_bucket).to(dev)
+        x = torch.from_numpy(w.x.view(np.int16)).to(dev)
+        wts = torch.from_numpy(w.weights).to(dev)
+        res = {"M": M}
+        for dedup in (False, True):
+            lay = moedl.alloc_layout(M, k, G, B, dedup, dev)
+            cap = lay.capacity
+            out = torch.empty((cap, N), dtype=torch.int16, device=dev)
+            y = torch.empty((M, N), dtype=torch.int16, device=dev)
+            eo = out
+            if dedup:   # combine reads slot-indexed rows: expand once, untimed
+                moedl.moe_layout_dispatch(idx, ebkt, B, True, x, lay=lay, out=out)
+                eo, _ = moedl.moe_expand(out, lay.send_row, lay.slot, M * k)
+
+            def three():
+                moedl.moe_dispatch_layout(idx, ebkt, B, dedup, out=lay)
+                moedl.moe_dispatch(x, lay.send_row, cap, out=out, dedup=dedup)
+                moedl.moe_combine(eo, wts, lay.slot, y=y)
+
+            def fused():
+                moedl.moe_layout_dispatch(idx, ebkt, B, dedup, x, lay=lay, out=out)
+                moedl.moe_combine(eo, wts, lay.slot, y=y)
+
+            tag = "dedup" if dedup else "flat"
+            for name, fn in (("three_calls", three), ("fused", fused)):
+                for _ in range(max(1, args.warmup)):
+                    fn()
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                for _ in range(args.steps):
+                    fn()
+                torch.cuda.synchronize()
+                res[f"{tag}_{name}_eager_us"] = round((time.perf_counter() - t0) * 1e6 / args.steps, 2)
+                res[f"{tag}_{name}_graph_us"] = round(graph_replay_us(torch, fn), 2)
+                xz = torch.where(x == -32768, torch.zeros_like(x), x)
+                assert bool((y == xz).all().item()), f"M={M} {tag} {name}: y != x"
+        rows.append(res)
+    head = rows[0]
+    out = {"metric": "small-M layout+dispatch+combine latency (graph replay, us per step)",
+           "value": head["flat_fused_graph_us"], "unit": "us", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "higher_is_better": False, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "uniform-top8-N7168-G256-B8", "M": [r["M"] for r in rows]},
+           "rows": rows}
+    print(json.dumps(out))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -339,6 +424,9 @@ def main():
     moedl.load()
     dev = torch.device("cuda:0")
     dedup = bool(args.dedup)
+    if args.path == "small":
+        bench_small(args, dev)
+        return
     w = workloads.make_workload(args.cfg)
     if args.path == "bucket":
         bench_bucket(args, w, dev)
@@ -349,6 +437,7 @@ def main():
     if args.path == "gemm":
         bench_gemm(args, w, dev)
         return
+
     M, N, G, k, B = w.M, w.N, w.G, w.k, w.B
     row_bytes = w.row_bytes
 

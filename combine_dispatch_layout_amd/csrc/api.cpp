@@ -85,6 +85,41 @@ moe_status moe_dispatch(const void* x, moe_dtype dtype, int64_t M, int32_t N,
                                          dedup, out, out_scale, out_rows, stream));
 }
 
+moe_status moe_layout_dispatch(const int32_t* topk_idx, int64_t M, int32_t k,
+                               const int32_t* expert_bucket, int32_t G, int32_t B, int32_t dedup,
+                               const void* x, moe_dtype dtype, int32_t N, const float* x_scale,
+                               int32_t* expert_count, int32_t* expert_offset,
+                               int32_t* bucket_count, int32_t* bucket_offset, int32_t* slot,
+                               int32_t* send_row, int32_t* send_token, int32_t* status,
+                               void* out, float* out_scale, int64_t out_rows,
+                               hipStream_t stream) {
+  const moe_status s = check_layout_sizes(M, k, G, B);
+  if (s != MOE_OK) return s;
+  if (N < 1 || out_rows < 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (dedup != 0 && dedup != 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (dtype != MOE_BF16 && dtype != MOE_FP8_E4M3) return MOE_ERR_INVALID_ARGUMENT;
+  if (M > MOE_FUSED_MAX_TOKENS) return MOE_ERR_UNSUPPORTED;
+  if (!expert_bucket || !expert_count || !expert_offset || !bucket_count || !bucket_offset ||
+      !status)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (M > 0 && (!topk_idx || !slot || !send_row || !send_token || !x))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if ((x_scale == nullptr) != (out_scale == nullptr)) return MOE_ERR_INVALID_ARGUMENT;
+  if (x_scale && dtype != MOE_FP8_E4M3) return MOE_ERR_INVALID_ARGUMENT;
+  const int64_t row_bytes = (int64_t)N * (dtype == MOE_BF16 ? 2 : 1);
+  if (row_bytes % 16 != 0) return MOE_ERR_UNSUPPORTED;
+  if (x_scale && N % MOE_SCALE_BLOCK != 0) return MOE_ERR_UNSUPPORTED;
+  if (out_rows > 0 && !out) return MOE_ERR_INVALID_ARGUMENT;
+  if ((x && !aligned16(x)) || (out && !aligned16(out))) return MOE_ERR_INVALID_ARGUMENT;
+  if (x_scale && (((uintptr_t)x_scale & 3u) || ((uintptr_t)out_scale & 3u)))
+    return MOE_ERR_INVALID_ARGUMENT;
+  const int32_t scale_cols = x_scale ? N / MOE_SCALE_BLOCK : 0;
+  return from_hip(moedl::launch_layout_dispatch(
+      topk_idx, M, k, expert_bucket, G, B, dedup, expert_count, expert_offset, bucket_count,
+      bucket_offset, slot, send_row, send_token, status, x, row_bytes, x_scale, scale_cols, out,
+      out_scale, out_rows, stream));
+}
+
 moe_status moe_combine(const uint16_t* expert_out, int64_t expert_rows, const float* weights,
                        const int32_t* slot, int64_t M, int32_t k, int32_t N, uint16_t* y,
                        hipStream_t stream) {

@@ -28,6 +28,8 @@
 // Kernels:
 //  - M <= 256 tokens (one tile): layout_single_kernel does everything in LDS in one
 //    launch.
+//  - M <= 512 with the row scatter in the same launch: layout_dispatch_small_kernel
+//    (every workgroup recomputes the layout in LDS, then copies its share of rows).
 //  - otherwise three launches, no inter-workgroup waiting and no initialised state:
 //    layout_tile_kernel (per-tile ranks and totals to the workspace),
 //    layout_scan_kernel (one 1024-thread workgroup scans each expert / bucket column
@@ -43,20 +45,89 @@ constexpr int kMaxE = MOE_MAX_EXPERTS;
 constexpr int kMaxB = MOE_MAX_BUCKETS;
 constexpr unsigned char kBadBucket = 0xFF;
 constexpr int kAbsent = -1;  // no entry (past the end, or an invalid id)
+constexpr int kExpertBits = 10;  // bits of an expert id (G <= 1024)
+constexpr int kBucketBits = 6;   // bits of a bucket id (B <= 64)
+static_assert(kMaxE <= (1 << kExpertBits) && kMaxB <= (1 << kBucketBits), "id widths");
 
 __device__ __forceinline__ int bits_for(int n) {  // bits needed for values in [0, n)
   return n <= 1 ? 0 : 32 - __builtin_clz((unsigned)(n - 1));
 }
 
-// Lanes of the wave whose `key` equals the caller's, among lanes with `ok` set.
-__device__ __forceinline__ uint64_t match_peers(bool ok, int key, int nbits) {
-  uint64_t peers = wave_ballot(ok);
-  for (int bit = 0; bit < nbits; ++bit) {
-    const bool set = (key >> bit) & 1;
-    const uint64_t bal = wave_ballot(ok && set);
-    peers &= set ? bal : ~bal;
+// Peer masks of C independent 64-entry chunks at once: peers[c] = the lanes whose
+// key[c] equals the caller's, among lanes with ok[c] set (meaningless where ok[c] is
+// false).  Lanes agree on a key when they agree on each of its nbits bits, one ballot
+// per bit.  The bit loop is outside the chunk loop and fully unrolled, so the ballots
+// of different chunks interleave instead of forming one long dependent chain.
+template <int C, int MAXBITS>
+__device__ __forceinline__ void match_peers(const bool (&ok)[C], const int (&key)[C], int nbits,
+                                            uint64_t (&peers)[C]) {
+#pragma unroll
+  for (int c = 0; c < C; ++c) peers[c] = wave_ballot(ok[c]);
+#pragma unroll
+  for (int bit = 0; bit < MAXBITS; ++bit) {
+    if (bit < nbits) {  // uniform
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        const bool set = (key[c] >> bit) & 1;
+        const uint64_t bal = wave_ballot(set);
+        peers[c] &= set ? bal : ~bal;
+      }
+    }
   }
-  return peers;
+}
+
+// Stable ranks of C chunks against per-key running counters in LDS (counter[key]).
+// For each chunk in order, one leader lane per distinct key adds the key's count in
+// the chunk with an LDS atomic that returns the previous value; a wave's LDS
+// operations complete in issue order, so that value counts exactly the earlier
+// chunks.  Peers fetch it from their leader (ds_bpermute) and add their rank among
+// the chunk's peers: rank[c] = entries with the same key before this one, in order
+// (chunk, lane).
+template <int C>
+__device__ __forceinline__ void stable_ranks(const bool (&ok)[C], const int (&key)[C],
+                                             const uint64_t (&peers)[C], int32_t* counter,
+                                             int (&rank)[C]) {
+  const int lane = threadIdx.x & 63;
+  int old[C];
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    old[c] = 0;
+    const int below = lanes_below(peers[c]);
+    if (ok[c] && below == 0) old[c] = atomicAdd(counter + key[c], __builtin_popcountll(peers[c]));
+    rank[c] = below;
+  }
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const int leader = ok[c] ? __builtin_ctzll(peers[c]) : lane;
+    rank[c] += __builtin_amdgcn_ds_bpermute(leader << 2, old[c]);
+  }
+}
+
+// The flat (t, j) entries of a tile are split over its waves in NC chunks of 64
+// entries each: wave w holds entries [tile * 256 * k + w * 64 * NC, + 64 * NC), chunk c
+// lane l being the entry at offset c * 64 + l.  NC = k rounded up to a power of two
+// covers a full tile; a single short tile (small M) takes the smallest NC that covers
+// it, so the work is spread over all waves with no idle chunks.
+template <int NC>
+__device__ __forceinline__ int64_t wave_first_entry(int tile, int32_t k, int w) {
+  return (int64_t)tile * kTileTokens * k + (int64_t)w * 64 * NC;
+}
+
+// Exclusive scan of src[0, n) into dst by one thread; dst[n] = the total when
+// with_total.  src may be dst.  For the short arrays here (n <= 64, usually a handful)
+// the independent LDS reads issue together, which beats a shuffle-based wave scan.
+// Callers put barriers around it.
+__device__ __forceinline__ void serial_exclusive_scan(const int32_t* src, int32_t* dst, int n,
+                                                      bool with_total) {
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int i = 0; i < n; ++i) {
+      const int v = src[i];
+      dst[i] = run;
+      run += v;
+    }
+    if (with_total) dst[n] = run;
+  }
 }
 
 template <int KC>  // KC: k rounded up to a power of two (chunks per wave)
@@ -69,27 +140,38 @@ struct TileLds {
   int32_t err_s;                          // first bad flat index in the tile
 };
 
-// Expert ranks of one 256-token tile.  On return (after a barrier): ec[c] / rc[c]
-// hold the expert id (or kAbsent) and the rank inside the tile of flat entry
-// wbase + c*64 + lane; totals[e] holds the tile's count of expert e (totals may be
-// global or LDS); lds.ids_s holds the tile's ids when keep_ids.
-template <int KC>
-__device__ void tile_expert_ranks(TileLds<KC>& lds, const int32_t* __restrict__ idx, int32_t M,
-                                  int32_t k, const int32_t* __restrict__ ebkt, int32_t G,
-                                  int32_t B, int tile, bool keep_ids, int32_t* totals,
-                                  int (&ec)[KC], int (&rc)[KC]) {
+// Last flat entry (exclusive) of a tile.
+__device__ __forceinline__ int64_t tile_end_entry(int32_t M, int32_t k, int tile) {
+  const int64_t Mk = (int64_t)M * k;
+  const int64_t e = ((int64_t)tile + 1) * kTileTokens * k;
+  return e < Mk ? e : Mk;
+}
+
+// Expert ranks of one 256-token tile, NC chunks per wave (see wave_first_entry).  On
+// return (after a barrier): ec[c] / rc[c] hold the expert id (or kAbsent) and the rank
+// inside the tile of flat entry wave_first_entry<NC>(tile, k, w) + c*64 + lane;
+// totals[e] holds the tile's count of expert e (totals may be global or LDS);
+// lds.ids_s holds the tile's ids (tile-local flat order) when keep_ids.
+template <int KC, int NC>
+__device__ __forceinline__ void tile_expert_ranks(TileLds<KC>& lds, const int32_t* __restrict__ idx,
+                                                  int32_t M, int32_t k,
+                                                  const int32_t* __restrict__ ebkt, int32_t G,
+                                                  int32_t B, int tile, bool keep_ids,
+                                                  int32_t* totals, int (&ec)[NC], int (&rc)[NC]) {
+  static_assert(NC <= KC, "a wave's chunks must fit the tile's id store");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = wave_index();
-  const int64_t Mk = (int64_t)M * k;
   const int nbits = bits_for(G);
-  const int64_t wbase = ((int64_t)tile * kTileTokens + (int64_t)w * 64) * k;
+  const int64_t wbase = wave_first_entry<NC>(tile, k, w);
+  const int64_t tend = tile_end_entry(M, k, tile);
+  const int local0 = w * 64 * NC;  // tile-local index of the wave's first entry
 
   // all global loads first: clamped, unconditional, so they are in flight together
 #pragma unroll
-  for (int c = 0; c < KC; ++c) {
+  for (int c = 0; c < NC; ++c) {
     const int64_t f = wbase + (int64_t)c * 64 + lane;
-    const bool valid = c < k && f < Mk;
+    const bool valid = f < tend;
     const int v = idx[valid ? f : 0];
     ec[c] = valid ? v : kAbsent;
   }
@@ -103,23 +185,21 @@ __device__ void tile_expert_ranks(TileLds<KC>& lds, const int32_t* __restrict__ 
   __syncthreads();
 
   int my_err = kNoError;
+  bool ok[NC];
 #pragma unroll
-  for (int c = 0; c < KC; ++c) {
+  for (int c = 0; c < NC; ++c) {
     int e = ec[c];
     if (e != kAbsent && (e < 0 || e >= G)) {
       my_err = min(my_err, (int)(wbase + c * 64 + lane));
       e = kAbsent;
     }
-    if (keep_ids && c < k) lds.ids_s[w * 64 * k + c * 64 + lane] = e;
-    const bool ok = e >= 0;
-    const uint64_t peers = match_peers(ok, e, nbits);
-    const int r = lanes_below(peers);
-    int old = 0;
-    if (ok) old = lds.wcnt[w][e];
-    if (ok && r == 0) lds.wcnt[w][e] = old + __builtin_popcountll(peers);
+    if (keep_ids) lds.ids_s[local0 + c * 64 + lane] = e;
+    ok[c] = e >= 0;
     ec[c] = e;
-    rc[c] = old + r;
   }
+  uint64_t peers[NC];
+  match_peers<NC, kExpertBits>(ok, ec, nbits, peers);
+  stable_ranks<NC>(ok, ec, peers, lds.wcnt[w], rc);
   if (my_err != kNoError) atomicMin(&lds.err_s, my_err);
   __syncthreads();
 
@@ -136,7 +216,7 @@ __device__ void tile_expert_ranks(TileLds<KC>& lds, const int32_t* __restrict__ 
   }
   __syncthreads();
 #pragma unroll
-  for (int c = 0; c < KC; ++c)
+  for (int c = 0; c < NC; ++c)
     if (ec[c] >= 0) rc[c] += lds.wcnt[w][ec[c]];
 }
 
@@ -145,7 +225,7 @@ __device__ void tile_expert_ranks(TileLds<KC>& lds, const int32_t* __restrict__ 
 // kBadBucket, dl[j] the token's rank among the tile's tokens that send to that
 // bucket; btotals[b] the tile's distinct-token count of bucket b.
 template <int KC>
-__device__ void tile_dedup_ranks(TileLds<KC>& lds, int32_t M, int32_t k, int32_t B, int tile,
+__device__ __forceinline__ void tile_dedup_ranks(TileLds<KC>& lds, int32_t M, int32_t k, int32_t B, int tile,
                                  int32_t* btotals, int (&eb)[KC], int (&dl)[KC]) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -206,14 +286,7 @@ __device__ int block_exclusive_scan(int v, int32_t* wave_sums /* >= NT/64 */) {
   }
   if (lane == 63) wave_sums[w] = incl;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int q = 0; q < NT / 64; ++q) {
-      const int s = wave_sums[q];
-      wave_sums[q] = run;
-      run += s;
-    }
-  }
+  serial_exclusive_scan(wave_sums, wave_sums, NT / 64, false);
   __syncthreads();
   const int r = wave_sums[w] + incl - v;
   __syncthreads();
@@ -248,20 +321,17 @@ __device__ void expert_order_offsets(OrderLds<NT>& lds, const unsigned char* map
   const int nbits = bits_for(B);
   int rk[CH];
   int bk[CH];
+  bool okc[CH];
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     const int e = w * per + c * 64 + lane;
-    const bool ok = c * 64 < per && e < G;
-    int b = ok ? (int)map_s[e] : 0;
-    b = b < B ? b : B - 1;  // a bad map entry is reported by status; keep it in range
-    const uint64_t peers = match_peers(ok, b, nbits);
-    const int r = lanes_below(peers);
-    int old = 0;
-    if (ok) old = lds.wbc[w][b];
-    if (ok && r == 0) lds.wbc[w][b] = old + __builtin_popcountll(peers);
-    rk[c] = old + r;
-    bk[c] = b;
+    okc[c] = c * 64 < per && e < G;
+    int b = okc[c] ? (int)map_s[e] : 0;
+    bk[c] = b < B ? b : B - 1;  // a bad map entry is reported by status; keep it in range
   }
+  uint64_t peers[CH];
+  match_peers<CH, kBucketBits>(okc, bk, nbits, peers);
+  stable_ranks<CH>(okc, bk, peers, lds.wbc[w], rk);
   __syncthreads();
   if (tid < B) {
     int run = 0;
@@ -273,14 +343,7 @@ __device__ void expert_order_offsets(OrderLds<NT>& lds, const unsigned char* map
     lds.base[tid] = run;
   }
   __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int b = 0; b < B; ++b) {
-      const int v = lds.base[b];
-      lds.base[b] = run;
-      run += v;
-    }
-  }
+  serial_exclusive_scan(lds.base, lds.base, B, false);
   __syncthreads();
   int pos[CH];
 #pragma unroll
@@ -319,7 +382,7 @@ __device__ void expert_order_offsets(OrderLds<NT>& lds, const unsigned char* map
 }
 
 // ------------------------------------------------------------------ M <= 256 tokens
-template <int KC>
+template <int KC, int NC>
 __global__ __launch_bounds__(kTileThreads) void layout_single_kernel(
     const int32_t* __restrict__ idx, int32_t M, int32_t k,
     const int32_t* __restrict__ ebkt, int32_t G, int32_t B, int32_t dedup,
@@ -343,8 +406,8 @@ __global__ __launch_bounds__(kTileThreads) void layout_single_kernel(
   if (tid < kMaxB) bsum_s[tid] = 0;
   if (tid == 0) mapbad_s = kNoError;
 
-  int ec[KC], rc[KC];
-  tile_expert_ranks<KC>(lds, idx, M, k, ebkt, G, B, 0, dedup != 0, cnt_s, ec, rc);
+  int ec[NC], rc[NC];
+  tile_expert_ranks<KC, NC>(lds, idx, M, k, ebkt, G, B, 0, dedup != 0, cnt_s, ec, rc);
   for (int e = tid; e < G; e += kTileThreads) {
     if (lds.map_s[e] == kBadBucket) atomicMin(&mapbad_s, e);
     else atomicAdd(&bsum_s[lds.map_s[e]], cnt_s[e]);
@@ -358,14 +421,7 @@ __global__ __launch_bounds__(kTileThreads) void layout_single_kernel(
     btot_s[tid] = bsum_s[tid];
   }
   __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int b = 0; b < B; ++b) {
-      boff_s[b] = run;
-      run += btot_s[b];
-    }
-    boff_s[B] = run;
-  }
+  serial_exclusive_scan(btot_s, boff_s, B, true);
   __syncthreads();
 
   for (int e = tid; e < G; e += kTileThreads) {
@@ -378,11 +434,11 @@ __global__ __launch_bounds__(kTileThreads) void layout_single_kernel(
     status[0] = mapbad_s != kNoError ? -(mapbad_s + 1)
                                      : (lds.err_s != kNoError ? lds.err_s + 1 : 0);
 
-  const int64_t wbase = (int64_t)w * 64 * k;
+  const int64_t wbase = wave_first_entry<NC>(0, k, w);
 #pragma unroll
-  for (int c = 0; c < KC; ++c) {
+  for (int c = 0; c < NC; ++c) {
     const int64_t f = wbase + (int64_t)c * 64 + lane;
-    if (c < k && f < Mk) {
+    if (f < Mk) {
       const int s = ec[c] >= 0 ? off_s[ec[c]] + rc[c] : -1;
       slot[f] = s;
       if (!dedup) {
@@ -407,6 +463,183 @@ __global__ __launch_bounds__(kTileThreads) void layout_single_kernel(
   }
 }
 
+// ------------------------------------------- layout + dispatch in one launch, M <= 512
+// The small-M regime is set by launches and the gaps between them, not by bytes, so
+// layout and row scatter share one launch.  Every workgroup computes the complete
+// layout of the (at most two) 256-token tiles in its own LDS with the building blocks
+// above.  The computation is deterministic, so all workgroups hold the same layout and
+// none ever waits for another; workgroup 0 alone writes the layout arrays.  Then the
+// workgroups share the row copies: work item i = (token, 4 KiB piece of its row) goes to
+// workgroup i mod gridDim.x, which loads the piece once (a batch of items at a time, all
+// loads in flight; the first batch is issued before the layout work, which hides its
+// latency) and stores it non-temporally to each of the token's distinct send rows
+// inside the buffer.  `idx` must be readable at index 0 even when M = 0.
+constexpr int kFusedPieceVecs = kTileThreads;  // 16-byte vectors per work item
+constexpr int kFusedBatch = 4;                  // work items loaded together
+constexpr int kFusedMaxBlocks = 256;            // one workgroup per CU
+
+template <int KC, int NTILE, int NC>
+__global__ __launch_bounds__(kTileThreads) void layout_dispatch_small_kernel(
+    const int32_t* __restrict__ idx, int32_t M, int32_t k,
+    const int32_t* __restrict__ ebkt, int32_t G, int32_t B, int32_t dedup,
+    int32_t* __restrict__ expert_count, int32_t* __restrict__ expert_offset,
+    int32_t* __restrict__ bucket_count, int32_t* __restrict__ bucket_offset,
+    int32_t* __restrict__ slot, int32_t* __restrict__ send_row,
+    int32_t* __restrict__ send_token, int32_t* __restrict__ status,
+    const u32x4* __restrict__ x, int32_t row_vecs, int32_t pieces,
+    const float* __restrict__ x_scale, int32_t scale_cols, u32x4* __restrict__ out,
+    float* __restrict__ out_scale, int64_t out_rows) {
+  __shared__ TileLds<KC> lds;
+  __shared__ OrderLds<kTileThreads> olds;
+  __shared__ int32_t tcnt_s[NTILE][kMaxE];  // per-tile expert counts
+  __shared__ int32_t cnt_s[kMaxE];
+  __shared__ int32_t off_s[kMaxE];
+  __shared__ int32_t tb_s[NTILE][kMaxB];    // per-tile distinct-token counts (dedup)
+  __shared__ int32_t bsum_s[kMaxB];
+  __shared__ int32_t btot_s[kMaxB];
+  __shared__ int32_t boff_s[kMaxB + 1];
+  __shared__ int32_t mapbad_s, err_s;
+  __shared__ int32_t row_s[NTILE * kTileTokens * KC];  // send row of flat entry t*k + j
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = wave_index();
+  const int64_t Mk = (int64_t)M * k;
+  const bool writer = blockIdx.x == 0;
+
+  // The rows do not depend on the layout: the first batch of row loads is issued
+  // now and lands while the layout is computed.
+  const int64_t items = (int64_t)M * pieces;
+  const int64_t stride = gridDim.x;
+  u32x4 v[kFusedBatch];
+  auto load_batch = [&](int64_t base) {
+#pragma unroll
+    for (int q = 0; q < kFusedBatch; ++q) {  // clamped, unconditional loads: all in flight
+      const int64_t it = base + q * stride;
+      const int64_t t = it < items ? it / pieces : 0;
+      const int c = (int)(it - t * pieces) * kFusedPieceVecs + tid;
+      const bool in_row = it < items && c < row_vecs;
+      v[q] = x[in_row ? t * row_vecs + c : 0];
+    }
+  };
+  if (items > 0) load_batch(blockIdx.x);  // uniform; x may be null only when M = 0
+
+  if (tid < kMaxB) bsum_s[tid] = 0;
+  if (tid == 0) {
+    mapbad_s = kNoError;
+    err_s = kNoError;
+  }
+
+  int ec[NTILE][NC], rc[NTILE][NC], eb[NTILE][KC], dl[NTILE][KC];
+#pragma unroll
+  for (int tile = 0; tile < NTILE; ++tile) {
+    if (tile > 0) __syncthreads();  // the previous tile's LDS reads are done
+    tile_expert_ranks<KC, NC>(lds, idx, M, k, ebkt, G, B, tile, dedup != 0, tcnt_s[tile], ec[tile],
+                          rc[tile]);
+    if (tid == 0) err_s = min(err_s, lds.err_s);
+    if (dedup) tile_dedup_ranks<KC>(lds, M, k, B, tile, tb_s[tile], eb[tile], dl[tile]);
+  }
+  __syncthreads();
+  for (int e = tid; e < G; e += kTileThreads) {
+    int c = tcnt_s[0][e];
+    if (NTILE > 1) c += tcnt_s[NTILE - 1][e];
+    cnt_s[e] = c;
+    if (lds.map_s[e] == kBadBucket) atomicMin(&mapbad_s, e);
+    else atomicAdd(&bsum_s[lds.map_s[e]], c);
+  }
+  expert_order_offsets<kTileThreads>(olds, lds.map_s, cnt_s, G, B, off_s);
+  if (tid < B) {
+    int bt = bsum_s[tid];
+    if (dedup) {
+      bt = tb_s[0][tid];
+      if (NTILE > 1) bt += tb_s[NTILE - 1][tid];
+    }
+    btot_s[tid] = bt;
+  }
+  __syncthreads();
+  serial_exclusive_scan(btot_s, boff_s, B, true);
+  __syncthreads();
+
+  if (writer) {
+    for (int e = tid; e < G; e += kTileThreads) {
+      expert_count[e] = cnt_s[e];
+      expert_offset[e] = off_s[e];
+    }
+    if (tid < B) bucket_count[tid] = btot_s[tid];
+    if (tid <= B) bucket_offset[tid] = boff_s[tid];
+    if (tid == 0)
+      status[0] = mapbad_s != kNoError ? -(mapbad_s + 1) : (err_s != kNoError ? err_s + 1 : 0);
+  }
+
+  const int64_t cap = dedup ? (int64_t)M * (k < B ? k : B) : Mk;
+#pragma unroll
+  for (int tile = 0; tile < NTILE; ++tile) {
+    const int64_t wbase = wave_first_entry<NC>(tile, k, w);
+    const int64_t tend = tile_end_entry(M, k, tile);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int64_t f = wbase + (int64_t)c * 64 + lane;
+      if (f < tend) {
+        const int e = ec[tile][c];
+        int s = -1;
+        if (e >= 0) s = off_s[e] + rc[tile][c] + (tile > 0 ? tcnt_s[0][e] : 0);
+        if (!dedup) row_s[f] = s;
+        if (writer) {
+          slot[f] = s;
+          if (!dedup) {
+            send_row[f] = s;
+            if (s >= 0 && s < Mk) send_token[s] = (int)(f / k);
+          }
+        }
+      }
+    }
+    if (dedup) {
+      const int t = tile * kTileTokens + w * 64 + lane;
+      if (t < M) {
+#pragma unroll
+        for (int j = 0; j < KC; ++j) {
+          if (j < k) {
+            const int b = eb[tile][j];
+            const int r = b != kBadBucket ? boff_s[b] + dl[tile][j] + (tile > 0 ? tb_s[0][b] : 0)
+                                          : -1;
+            row_s[t * k + j] = r;
+            if (writer) {
+              send_row[(int64_t)t * k + j] = r;
+              if (r >= 0 && r < cap) send_token[r] = t;
+            }
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // row scatter
+  for (int64_t base = blockIdx.x; base < items; base += stride * kFusedBatch) {
+    if (base != (int64_t)blockIdx.x) load_batch(base);
+#pragma unroll
+    for (int q = 0; q < kFusedBatch; ++q) {
+      const int64_t it = base + q * stride;
+      if (it >= items) break;  // uniform
+      const int t = (int)(it / pieces);
+      const int piece = (int)(it - (int64_t)t * pieces);
+      const int c = piece * kFusedPieceVecs + tid;
+      const int32_t* rows = row_s + t * k;
+      for (int j = 0; j < k; ++j) {
+        const int r = rows[j];
+        bool first = r >= 0 && r < out_rows;
+        for (int jj = 0; jj < j; ++jj) first = first && rows[jj] != r;
+        if (!first) continue;  // uniform
+        if (c < row_vecs) __builtin_nontemporal_store(v[q], out + (int64_t)r * row_vecs + c);
+        if (x_scale != nullptr && piece == 0) {
+          for (int sc = tid; sc < scale_cols; sc += kTileThreads)
+            out_scale[(int64_t)r * scale_cols + sc] = x_scale[(int64_t)t * scale_cols + sc];
+        }
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ M > 256 tokens
 template <int KC>
 __global__ __launch_bounds__(kTileThreads) void layout_tile_kernel(
@@ -419,15 +652,15 @@ __global__ __launch_bounds__(kTileThreads) void layout_tile_kernel(
   const int tile = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int w = wave_index();
-  const int64_t Mk = (int64_t)M * k;
   int ec[KC], rc[KC];
-  tile_expert_ranks<KC>(lds, idx, M, k, ebkt, G, B, tile, dedup != 0,
-                        tile_hist + (int64_t)tile * G, ec, rc);
-  const int64_t wbase = ((int64_t)tile * kTileTokens + (int64_t)w * 64) * k;
+  tile_expert_ranks<KC, KC>(lds, idx, M, k, ebkt, G, B, tile, dedup != 0,
+                            tile_hist + (int64_t)tile * G, ec, rc);
+  const int64_t wbase = wave_first_entry<KC>(tile, k, w);
+  const int64_t tend = tile_end_entry(M, k, tile);
 #pragma unroll
   for (int c = 0; c < KC; ++c) {
     const int64_t f = wbase + (int64_t)c * 64 + lane;
-    if (c < k && f < Mk) slot_local[f] = ec[c] >= 0 ? rc[c] : -1;
+    if (f < tend) slot_local[f] = ec[c] >= 0 ? rc[c] : -1;
   }
   if (dedup) {
     int eb[KC], dl[KC];
@@ -556,15 +789,21 @@ __global__ __launch_bounds__(kScanThreads) void layout_scan_kernel(
     if (tid < B) btot_s[tid] = bsum_s[tid];
     __syncthreads();
   }
-  if (tid == 0) {
-    int run = 0;
-    for (int b = 0; b < B; ++b) {
-      bucket_count[b] = btot_s[b];
-      bucket_offset[b] = run;
-      run += btot_s[b];
+  if (tid < 64) {  // bucket counts and their exclusive scan, one wave
+    const int v = tid < B ? btot_s[tid] : 0;
+    int incl = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(incl, d, 64);
+      if (tid >= d) incl += o;
     }
-    bucket_offset[B] = run;
-    status[0] = mapbad_s != kNoError ? -(mapbad_s + 1) : (err_s != kNoError ? err_s + 1 : 0);
+    if (tid < B) {
+      bucket_count[tid] = v;
+      bucket_offset[tid] = incl - v;
+    }
+    if (tid == 63) bucket_offset[B] = incl;
+    if (tid == 0)
+      status[0] = mapbad_s != kNoError ? -(mapbad_s + 1) : (err_s != kNoError ? err_s + 1 : 0);
   }
 }
 
@@ -604,6 +843,12 @@ __global__ __launch_bounds__(256) void layout_finalize_kernel(
   if (r >= 0 && r < send_cap) send_token[r] = t;
 }
 
+// Chunks of 64 entries per wave that cover one tile of `entries` entries with all
+// four waves (rounded up to a power of two by the callers' instantiations).
+inline int chunks_per_wave(int64_t entries) {
+  return (int)((entries + kTileThreads - 1) / kTileThreads);
+}
+
 template <int KC>
 void launch_tiles(const int32_t* topk_idx, int64_t M, int32_t k, const int32_t* expert_bucket,
                   int32_t G, int32_t B, int32_t dedup, int32_t* expert_count,
@@ -613,9 +858,17 @@ void launch_tiles(const int32_t* topk_idx, int64_t M, int32_t k, const int32_t* 
   const int T = (int)layout_tiles(M);
   const int64_t Mk = M * k;
   if (T == 1) {
-    hipLaunchKernelGGL(layout_single_kernel<KC>, dim3(1), dim3(kTileThreads), 0, stream, topk_idx,
-                       (int32_t)M, k, expert_bucket, G, B, dedup, expert_count, expert_offset,
-                       bucket_count, bucket_offset, slot, send_row, send_token, status);
+#define MOEDL_SINGLE(NC)                                                                        \
+  hipLaunchKernelGGL((layout_single_kernel<KC, NC>), dim3(1), dim3(kTileThreads), 0, stream,        \
+                     topk_idx, (int32_t)M, k, expert_bucket, G, B, dedup, expert_count,            \
+                     expert_offset, bucket_count, bucket_offset, slot, send_row, send_token, status)
+    const int nc = chunks_per_wave(Mk);
+    if (nc <= 1 || KC == 1) MOEDL_SINGLE(1);
+    else if (nc <= 2 || KC == 2) MOEDL_SINGLE(KC >= 2 ? 2 : 1);
+    else if (nc <= 4 || KC == 4) MOEDL_SINGLE(KC >= 4 ? 4 : 1);
+    else if (nc <= 8 || KC == 8) MOEDL_SINGLE(KC >= 8 ? 8 : 1);
+    else MOEDL_SINGLE(KC >= 16 ? 16 : 1);
+#undef MOEDL_SINGLE
     return;
   }
   if (T > 1) {
@@ -633,6 +886,39 @@ void launch_tiles(const int32_t* topk_idx, int64_t M, int32_t k, const int32_t* 
                        ws.tile_bhist, expert_offset, bucket_offset, slot, send_row, send_token,
                        dedup ? M * (int64_t)(k < B ? k : B) : Mk);
   }
+}
+
+template <int KC>
+hipError_t launch_fused(const int32_t* topk_idx, int64_t M, int32_t k, const int32_t* expert_bucket,
+                        int32_t G, int32_t B, int32_t dedup, int32_t* expert_count,
+                        int32_t* expert_offset, int32_t* bucket_count, int32_t* bucket_offset,
+                        int32_t* slot, int32_t* send_row, int32_t* send_token, int32_t* status,
+                        const void* x, int64_t row_bytes, const float* x_scale,
+                        int32_t scale_cols, void* out, float* out_scale, int64_t out_rows,
+                        hipStream_t stream) {
+  const int32_t row_vecs = (int32_t)(row_bytes / 16);
+  const int32_t pieces = (row_vecs + kFusedPieceVecs - 1) / kFusedPieceVecs;
+  const int64_t items = M * pieces;
+  const unsigned grid = (unsigned)(items < 1 ? 1 : (items < kFusedMaxBlocks ? items : kFusedMaxBlocks));
+  const int32_t* idx = M > 0 ? topk_idx : expert_bucket;  // read at index 0 only
+#define MOEDL_FUSED(NT, NC)                                                                     \
+  hipLaunchKernelGGL((layout_dispatch_small_kernel<KC, NT, NC>), dim3(grid), dim3(kTileThreads), 0, \
+                     stream, idx, (int32_t)M, k, expert_bucket, G, B, dedup, expert_count,         \
+                     expert_offset, bucket_count, bucket_offset, slot, send_row, send_token,      \
+                     status, (const u32x4*)x, row_vecs, pieces, x_scale, scale_cols, (u32x4*)out, \
+                     out_scale, out_rows)
+  if (M > kTileTokens) {
+    MOEDL_FUSED(2, KC);
+  } else {
+    const int nc = chunks_per_wave(M * k);
+    if (nc <= 1 || KC == 1) MOEDL_FUSED(1, 1);
+    else if (nc <= 2 || KC == 2) MOEDL_FUSED(1, KC >= 2 ? 2 : 1);
+    else if (nc <= 4 || KC == 4) MOEDL_FUSED(1, KC >= 4 ? 4 : 1);
+    else if (nc <= 8 || KC == 8) MOEDL_FUSED(1, KC >= 8 ? 8 : 1);
+    else MOEDL_FUSED(1, KC >= 16 ? 16 : 1);
+  }
+#undef MOEDL_FUSED
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -672,6 +958,31 @@ hipError_t launch_layout(const int32_t* topk_idx, int64_t M, int32_t k,
   else launch_tiles<16>(MOEDL_ARGS);
 #undef MOEDL_ARGS
   return hipGetLastError();
+}
+
+}  // namespace moedl
+
+namespace moedl {
+
+hipError_t launch_layout_dispatch(const int32_t* topk_idx, int64_t M, int32_t k,
+                                  const int32_t* expert_bucket, int32_t G, int32_t B,
+                                  int32_t dedup, int32_t* expert_count, int32_t* expert_offset,
+                                  int32_t* bucket_count, int32_t* bucket_offset, int32_t* slot,
+                                  int32_t* send_row, int32_t* send_token, int32_t* status,
+                                  const void* x, int64_t row_bytes, const float* x_scale,
+                                  int32_t scale_cols, void* out, float* out_scale,
+                                  int64_t out_rows, hipStream_t stream) {
+  if (M > kFusedMaxTokens) return hipErrorInvalidValue;
+#define MOEDL_ARGS                                                                          \
+  topk_idx, M, k, expert_bucket, G, B, dedup, expert_count, expert_offset, bucket_count,    \
+      bucket_offset, slot, send_row, send_token, status, x, row_bytes, x_scale, scale_cols, \
+      out, out_scale, out_rows, stream
+  if (k <= 1) return launch_fused<1>(MOEDL_ARGS);
+  if (k <= 2) return launch_fused<2>(MOEDL_ARGS);
+  if (k <= 4) return launch_fused<4>(MOEDL_ARGS);
+  if (k <= 8) return launch_fused<8>(MOEDL_ARGS);
+  return launch_fused<16>(MOEDL_ARGS);
+#undef MOEDL_ARGS
 }
 
 }  // namespace moedl

@@ -37,6 +37,16 @@ hipError_t launch_layout(const int32_t* topk_idx, int64_t M, int32_t k,
                          int32_t* send_row, int32_t* send_token, int32_t* status,
                          const LayoutWorkspace& ws, hipStream_t stream);
 
+constexpr int kFusedMaxTokens = MOE_FUSED_MAX_TOKENS;  // layout + dispatch in one launch
+hipError_t launch_layout_dispatch(const int32_t* topk_idx, int64_t M, int32_t k,
+                                  const int32_t* expert_bucket, int32_t G, int32_t B,
+                                  int32_t dedup, int32_t* expert_count, int32_t* expert_offset,
+                                  int32_t* bucket_count, int32_t* bucket_offset, int32_t* slot,
+                                  int32_t* send_row, int32_t* send_token, int32_t* status,
+                                  const void* x, int64_t row_bytes, const float* x_scale,
+                                  int32_t scale_cols, void* out, float* out_scale,
+                                  int64_t out_rows, hipStream_t stream);
+
 hipError_t launch_dispatch(const void* x, int64_t M, int64_t row_bytes,
                            const float* x_scale, int32_t scale_cols,
                            const int32_t* send_row, int32_t k, int32_t dedup, void* out,

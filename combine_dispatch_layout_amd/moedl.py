@@ -43,6 +43,9 @@ SIGNATURES = {
         _i32p, _i32p, _i32p, _vp, ctypes.c_size_t, _vp]),
     "moe_dispatch": (ctypes.c_int, [
         _vp, ctypes.c_int, _i64, _i32, _vp, _i32p, _i32, _i32, _vp, _vp, _i64, _vp]),
+    "moe_layout_dispatch": (ctypes.c_int, [
+        _i32p, _i64, _i32, _i32p, _i32, _i32, _i32, _vp, ctypes.c_int, _i32, _vp, _i32p, _i32p,
+        _i32p, _i32p, _i32p, _i32p, _i32p, _i32p, _vp, _vp, _i64, _vp]),
     "moe_combine": (ctypes.c_int, [_vp, _i64, _vp, _i32p, _i64, _i32, _i32, _vp, _vp]),
     "moe_expand": (ctypes.c_int, [
         _vp, ctypes.c_int, _i64, _i32, _vp, _i32p, _i32p, _i64, _i32, _vp, _vp, _i64, _vp]),
@@ -190,6 +193,36 @@ def moe_dispatch(x: torch.Tensor, send_row: torch.Tensor, out_rows: int,
                             int(dedup), _ptr(out), _ptr(out_scale), out_rows, _stream(stream))
     _check("moe_dispatch", st)
     return out, out_scale
+
+
+FUSED_MAX_TOKENS = 512
+
+
+def moe_layout_dispatch(topk_idx: torch.Tensor, expert_bucket: torch.Tensor, B: int,
+                        dedup: bool, x: torch.Tensor, x_scale: Optional[torch.Tensor] = None,
+                        lay: Optional[Layout] = None, out: Optional[torch.Tensor] = None,
+                        out_scale: Optional[torch.Tensor] = None, stream=None):
+    """moe_dispatch_layout + moe_dispatch in one launch (M <= 512) -> (Layout, out,
+    out_scale).  The Layout's workspace is not used."""
+    M, k = topk_idx.shape
+    G = expert_bucket.shape[0]
+    N = x.shape[1]
+    if topk_idx.dtype != torch.int32 or expert_bucket.dtype != torch.int32:
+        raise TypeError("topk_idx and expert_bucket must be int32")
+    if lay is None:
+        lay = alloc_layout(M, k, G, B, dedup, topk_idx.device)
+    rows = lay.capacity
+    if out is None:
+        out = torch.empty((rows, N), dtype=x.dtype, device=x.device)
+    if x_scale is not None and out_scale is None:
+        out_scale = torch.empty((rows, x_scale.shape[1]), dtype=torch.float32, device=x.device)
+    st = lib().moe_layout_dispatch(
+        _ptr(topk_idx), M, k, _ptr(expert_bucket), G, B, int(dedup), _ptr(x), _dtype_code(x), N,
+        _ptr(x_scale), _ptr(lay.expert_count), _ptr(lay.expert_offset), _ptr(lay.bucket_count),
+        _ptr(lay.bucket_offset), _ptr(lay.slot), _ptr(lay.send_row), _ptr(lay.send_token),
+        _ptr(lay.status), _ptr(out), _ptr(out_scale), out.shape[0], _stream(stream))
+    _check("moe_layout_dispatch", st)
+    return lay, out, out_scale
 
 
 def moe_combine(expert_out: torch.Tensor, weights: torch.Tensor, slot: torch.Tensor,

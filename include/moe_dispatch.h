@@ -155,6 +155,30 @@ moe_status moe_dispatch(const void* x, moe_dtype dtype, int64_t M, int32_t N,
                         hipStream_t stream);
 
 /*
+ * moe_layout_dispatch -- moe_dispatch_layout followed by moe_dispatch, in one launch,
+ * for small batches (M <= MOE_FUSED_MAX_TOKENS).
+ *
+ * The small-token regime of "All2all performance comparison between Triton-distributed
+ * and DeepEP" ("Results (Latency in us)" and the note under it: at 128 tokens the
+ * dispatch is a few tens of microseconds, so launch count and gaps, not bytes, decide
+ * it).  Every output is the one the two calls would produce: the layout arrays and
+ * status word of moe_dispatch_layout (same arguments, same meaning) and the send rows
+ * of moe_dispatch (x, dtype, N, x_scale, out, out_scale, out_rows as there).  No
+ * workspace is needed.  Within the launch every workgroup derives the layout in its
+ * own on-chip memory, so no workgroup waits for another.
+ * Errors: those of the two calls, and MOE_ERR_UNSUPPORTED for M > MOE_FUSED_MAX_TOKENS.
+ */
+#define MOE_FUSED_MAX_TOKENS 512
+moe_status moe_layout_dispatch(const int32_t* topk_idx, int64_t M, int32_t k,
+                               const int32_t* expert_bucket, int32_t G, int32_t B, int32_t dedup,
+                               const void* x, moe_dtype dtype, int32_t N, const float* x_scale,
+                               int32_t* expert_count, int32_t* expert_offset,
+                               int32_t* bucket_count, int32_t* bucket_offset, int32_t* slot,
+                               int32_t* send_row, int32_t* send_token, int32_t* status,
+                               void* out, float* out_scale, int64_t out_rows,
+                               hipStream_t stream);
+
+/*
  * moe_combine -- routing-weighted top-k sum of expert outputs back in token order.
  *
  *   y[t, i] = bf16_rne( sum_{j=0..k-1} w[t, j] * expert_out[slot[t, j], i] )

@@ -198,3 +198,23 @@ def test_grouped_gemm_argument_errors(kw, status):
     lib = moedl.load()
     assert lib.moe_grouped_gemm(a["x"], a["rows"], a["K"], a["w"], a["G"], a["Nout"], a["te"],
                                 a["tr"], a["tn"], a["mt"], a["y"], None) == status
+
+
+def fused_call(idx=P, M=64, k=8, eb=P, G=256, B=8, dd=0, x=P, dtype=0, N=7168, xs=None, o=P,
+               st=P, out=P, os_=None, rows=512):
+    return moedl.load().moe_layout_dispatch(idx, M, k, eb, G, B, dd, x, dtype, N, xs, o, o, o, o,
+                                            o, o, o, st, out, os_, rows, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=-1), INVALID), (dict(k=0), INVALID), (dict(k=9, G=8), INVALID), (dict(N=0), INVALID),
+    (dict(rows=-1), INVALID), (dict(dd=2), INVALID), (dict(dtype=2), INVALID),
+    (dict(idx=None), INVALID), (dict(eb=None), INVALID), (dict(o=None), INVALID),
+    (dict(st=None), INVALID), (dict(x=None), INVALID), (dict(out=None), INVALID),
+    (dict(x=P + 4), INVALID), (dict(out=P + 8), INVALID), (dict(xs=P), INVALID),
+    (dict(xs=P, os_=P), INVALID), (dict(M=513), UNSUPPORTED), (dict(k=17, G=64), UNSUPPORTED),
+    (dict(G=1025), UNSUPPORTED), (dict(B=65), UNSUPPORTED), (dict(N=7164), UNSUPPORTED),
+    (dict(dtype=1, N=7184, xs=P, os_=P), UNSUPPORTED),
+])
+def test_layout_dispatch_argument_errors(kw, status):
+    assert fused_call(**kw) == status
