@@ -226,7 +226,8 @@ moe_status moe_grouped_gemm(const uint16_t* x, int64_t rows, int32_t K, const ui
                             int32_t max_tiles, uint16_t* y, hipStream_t stream) {
   if (rows < 0 || K < 1 || G < 1 || Nout < 1 || max_tiles < 0) return MOE_ERR_INVALID_ARGUMENT;
   if (K % 64 != 0 || Nout % 128 != 0) return MOE_ERR_UNSUPPORTED;
-  if ((int64_t)max_tiles * (Nout / 128) > (int64_t)1 << 23) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)MOE_GEMM_TILE_M * K * 2 > 0x7FFFFFFF) return MOE_ERR_UNSUPPORTED;  // 32-bit offsets
+  if ((int64_t)max_tiles * (Nout / 128) > (int64_t)1 << 23) return MOE_ERR_UNSUPPORTED;  // grid
   if (!w || (max_tiles > 0 && (!tile_expert || !tile_row0 || !tile_rows))) return MOE_ERR_INVALID_ARGUMENT;
   if (rows > 0 && (!x || !y)) return MOE_ERR_INVALID_ARGUMENT;
   if ((x && !aligned16(x)) || !aligned16(w)) return MOE_ERR_INVALID_ARGUMENT;

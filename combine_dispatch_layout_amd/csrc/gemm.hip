@@ -13,29 +13,33 @@
 // in ascending id, tile_m rows each, the last shorter); unused entries of the tile
 // arrays get expert -1 so a GEMM grid sized by the host-side bound simply exits there.
 //
-// grouped_gemm_kernel: one 256-thread workgroup per (row tile, 128-column block).
-//  - Grid: one linear index, column blocks fastest (max_tiles * Nout / 128 groups).
+// grouped_gemm_kernel: one 256-thread workgroup per (row tile, column block of 256, or of
+// 128 when Nout is not a multiple of 256).
+//  - Grid: one linear index over max_tiles * Nout / BN workgroups, mapped to (row tile,
+//    column block) by gemm_block_order (XCD-aware, grouped).
 //  - Both operands are K-contiguous ([rows, K] and [Nout, K]), which is what an MFMA
 //    lane needs: 8 consecutive k of one row / one column.
-//  - Per 64-wide k step the workgroup stages a 128 x 64 tile of x and of w in LDS
-//    (rows padded to 72 bf16 so the 16-byte fragment reads of 8 consecutive rows hit
-//    distinct bank groups), while the next step's tiles are already loading into
-//    registers.
-//  - The four waves form a 2 x 2 grid of 64 x 64 output blocks; each wave runs
-//    2 x 2 v_mfma_f32_32x32x16_bf16 per 16-wide k slice (64 fp32 accumulators per
-//    lane).  Accumulator lane layout (verified on the GPU): value v of lane l is
-//    C[8*(v/4) + 4*(l/32) + v%4][l%32]; operand lane l holds A[l%32][8*(l/32) + i] and
-//    B[8*(l/32) + i][l%32].
+//  - Per 64-wide k step the workgroup stages the tile's 128 x 64 x values and BN x 64
+//    weights in one of two LDS buffers (rows padded to 72 bf16 so the 16-byte fragment
+//    reads of consecutive rows hit distinct bank groups); the next step's global loads
+//    are in flight in registers meanwhile; one barrier per step.
+//  - 2 * BN / 64 waves (8 for BN = 256) form a 2 x BN/64 grid of 64 x 64 output blocks;
+//    each wave runs 2 x 2 v_mfma_f32_32x32x16_bf16 per 16-wide k slice.  Accumulator lane layout
+//    (verified on the GPU): value v of lane l is C[8*(v/4) + 4*(l/32) + v%4][l%32];
+//    operand lane l holds A[l%32][8*(l/32) + i] and B[8*(l/32) + i][l%32].
 //  - Rows past the tile's end read as zero and are not stored.
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moedl {
 namespace {
 
-constexpr int kBM = 128;
-constexpr int kBN = 128;
-constexpr int kBK = 64;
-constexpr int kPadK = kBK + 8;  // LDS row pitch in bf16
+constexpr int kBM = 128;   // rows per tile (one tile of moe_grouped_gemm_tiles)
+constexpr int kBK = 64;    // k per pipeline step
+constexpr int kBufferWord3 = 0x00020000;  // raw buffer resource: no format, no swizzle
+constexpr int kPadK = kBK + 8;  // LDS row pitch in bf16: 16-byte fragment reads of
+                                // consecutive rows land in distinct bank groups
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -84,93 +88,190 @@ __global__ __launch_bounds__(1024) void gemm_tiles_kernel(
   for (int t = total_s + tid; t < max_tiles; t += 1024) tile_expert[t] = -1;
 }
 
-__global__ __launch_bounds__(256) void grouped_gemm_kernel(
+// Workgroup -> (row tile, column block).  The hardware hands workgroup b to XCD b % 8,
+// round robin; each XCD has its own L2.  So the logical order is cut into 8 contiguous
+// ranges, one per XCD, and within a range the blocks go in groups of kGroupTiles
+// consecutive row tiles (mostly of one expert), column block outermost: the blocks in
+// flight on an XCD share one weight slice and a few x tiles, both streamed along K
+// together, and an expert's weights are read by one or two XCDs instead of all eight.
+constexpr int kGroupTiles = 8;
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ void gemm_block_order(int bid, int nwg, int nblk, int* tile,
+                                                 int* jblk) {
+  const int xcd = bid % kXcds;
+  const int per = nwg / kXcds, rem = nwg % kXcds;
+  const int L = xcd * per + min(xcd, rem) + bid / kXcds;  // logical block index
+  const int group = L / (kGroupTiles * nblk);
+  const int first = group * kGroupTiles;
+  const int max_tiles = nwg / nblk;
+  const int gsize = min(kGroupTiles, max_tiles - first);
+  const int r = L - group * kGroupTiles * nblk;
+  *jblk = r / gsize;
+  *tile = first + r % gsize;
+}
+
+// One workgroup = one BM-row tile (BM = 256) x BN columns (BN = 256, or 128 when Nout is
+// not a multiple of 256), 2 * BN / 64 waves: wave (wm, wn) owns the BM/2 x 64 output
+// block at rows wm*BM/2, columns wn*64, i.e. BM/64 x 2 accumulator blocks of 32 x 32.
+// With BN = 256 that is 8 waves, two per SIMD.
+// A 256 x 256 tile moves (256 + 256) * 64 * 2 bytes per 64-wide k step for 2 * 256 *
+// 256 * 64 flops, a third fewer bytes per flop than 128 x 256: the global -> LDS path
+// bounds this kernel, not the matrix cores (measured: without the per-step loads and
+// LDS writes it runs at ~1.97 PFLOP/s).
+// Short tiles (an expert's last rows): x is read through a buffer resource whose size
+// ends at the tile's last row, so rows past the end come back as zeros with no memory
+// traffic and every load stays unconditional.  (Skipping the MFMAs of 32-row blocks
+// past the end was measured slower: the branch splits the MFMA / load interleave.)
+// Per 64-wide k step s: the MFMAs read LDS buffer s%2 (fragments double-buffered in
+// registers across the four 16-wide k slices) while the tile of step s+1, loaded into
+// registers during step s-1, is written to buffer (s+1)%2 and the tile of step s+2 is
+// loaded.  A wave issues in order, so those LDS writes and global loads are placed
+// between the MFMA groups of the k slices (sched_barrier fences keep them there): the
+// address unit then works while the matrix cores do.  Issued after all of a step's
+// MFMAs instead, they form one burst per step that the matrix cores wait through.  The
+// loop body has no branches (the last two steps are peeled), which keeps the compiler's
+// memory wait counts exact.  One barrier per step orders the two LDS buffers.
+template <int BM, int BN>
+__global__ __launch_bounds__(2 * BN) void grouped_gemm_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wgt, int32_t K, int32_t Nout,
     const int32_t* __restrict__ tile_expert, const int32_t* __restrict__ tile_row0,
     const int32_t* __restrict__ tile_rows, uint16_t* __restrict__ y) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[kBM * kPadK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[kBN * kPadK];
-  // one linear grid, column blocks fastest: the workgroups of one row tile are
-  // dispatched back to back and share its x rows in cache
-  const int nblk = Nout / kBN;
-  const int tile = blockIdx.x / nblk;
+  constexpr int NT = 2 * BN;                // threads
+  constexpr int RS = NT / 8;                // rows staged per pass (8 threads per row)
+  constexpr int AP = BM / RS;               // x rows per thread per step
+  constexpr int BP = BN / RS;               // w rows per thread per step
+  constexpr int WR = BM / 2;                // rows per wave
+  constexpr int I = WR / 32, J = 2;         // 32 x 32 blocks per wave
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * kPadK];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * kPadK];
+
+  int tile, jblk;
+  gemm_block_order(blockIdx.x, gridDim.x, Nout / BN, &tile, &jblk);
   const int e = tile_expert[tile];
   if (e < 0) return;  // uniform: past the last tile
   const int r0 = tile_row0[tile];
-  const int nrows = min(tile_rows[tile], kBM);
-  const int n0 = (blockIdx.x - tile * nblk) * kBN;
+  const int nrows = min(tile_rows[tile], BM);
+  const int n0 = jblk * BN;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = wave_index();
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w & 1, wn = w >> 1;
 
-  const uint16_t* xa = x + (int64_t)r0 * K;
+  // x through a buffer resource ending at the tile's last row: loads past it read 0
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(x + (int64_t)r0 * K), (short)0, nrows * K * 2, kBufferWord3);
   const uint16_t* wb = wgt + ((int64_t)e * Nout + n0) * K;
 
-  // global -> register staging: 4 rows x 16 bytes of A and of B per thread per step
-  const int lrow = tid >> 3;        // 0..31
-  const int lcol = (tid & 7) * 8;   // bf16 column of the 16-byte chunk
-  u32x4 ra[4], rb[4];
-  auto load_tiles = [&](int k0) {
+  // global -> register staging: thread t moves the 16-byte chunk (t % 8) of rows
+  // t / 8 + RS p; eight consecutive threads cover one row's 128 bytes
+  const int lrow = tid >> 3;
+  const int lcol = (tid & 7) * 8;
+  u32x4 ra[AP], rb[BP];
+  auto load_a = [&](int k0) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int row = lrow + p * 32;
-      const int rc = row < nrows ? row : nrows - 1;  // clamped: the load is unconditional
-      ra[p] = *(const u32x4*)(xa + (int64_t)rc * K + k0 + lcol);
-      rb[p] = *(const u32x4*)(wb + (int64_t)row * K + k0 + lcol);
+    for (int p = 0; p < AP; ++p) {
+      const int row = lrow + p * RS;
+      ra[p] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, (row * K + k0 + lcol) * 2, 0, 0));
     }
   };
-  auto store_tiles = [&]() {
+  auto load_b = [&](int k0, int p0, int p1) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int row = lrow + p * 32;
-      *(u32x4*)(As + row * kPadK + lcol) = row < nrows ? ra[p] : (u32x4){0u, 0u, 0u, 0u};
-      *(u32x4*)(Bs + row * kPadK + lcol) = rb[p];
-    }
+    for (int p = 0; p < BP; ++p)
+      if (p >= p0 && p < p1) rb[p] = *(const u32x4*)(wb + (int64_t)(lrow + p * RS) * K + k0 + lcol);
+  };
+  auto store_a = [&](int buf) {
+#pragma unroll
+    for (int p = 0; p < AP; ++p) *(u32x4*)(&As[buf][(lrow + p * RS) * kPadK + lcol]) = ra[p];
+  };
+  auto store_b = [&](int buf) {
+#pragma unroll
+    for (int p = 0; p < BP; ++p) *(u32x4*)(&Bs[buf][(lrow + p * RS) * kPadK + lcol]) = rb[p];
   };
 
-  f32x16_t acc[2][2];
+  f32x16_t acc[I][J];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < I; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = (f32x16_t){};
+    for (int j = 0; j < J; ++j) acc[i][j] = (f32x16_t){};
 
-  load_tiles(0);
-  for (int k0 = 0; k0 < K; k0 += kBK) {
-    __syncthreads();  // previous step's fragments are consumed
-    store_tiles();
-    __syncthreads();
-    if (k0 + kBK < K) load_tiles(k0 + kBK);  // in flight during the MFMAs below
-#pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      const int kc = kk * 16 + (lane >> 5) * 8;
-      bf16x8_t af[2], bfr[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int row = wm * 64 + i * 32 + (lane & 31);
-        af[i] = *(const bf16x8_t*)(As + row * kPadK + kc);
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int col = wn * 64 + j * 32 + (lane & 31);
-        bfr[j] = *(const bf16x8_t*)(Bs + col * kPadK + kc);
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
+  const int steps = K / kBK;
+  load_a(0);
+  load_b(0, 0, BP);
+  store_a(0);
+  store_b(0);
+  if (steps > 1) {
+    load_a(kBK);
+    load_b(kBK, 0, BP);
   }
+  __syncthreads();
+  // One k step.  NEXT: the tile of step s+1 is written to the other buffer; NEXT2: the
+  // tile of step s+2 is loaded.  The steady-state loop runs with both set and no
+  // branches in its body, so the compiler's wait counts stay exact; the last two steps
+  // are peeled.
+  auto step = [&](int s, auto next_c, auto next2_c) {
+    constexpr bool NEXT = decltype(next_c)::value;
+    constexpr bool NEXT2 = decltype(next2_c)::value;
+    const int buf = s & 1;
+    const int k2 = (s + 2) * kBK;
+    const uint16_t* Ab = As[buf] + (wm * WR + (lane & 31)) * kPadK + (lane >> 5) * 8;
+    const uint16_t* Bb = Bs[buf] + (wn * 64 + (lane & 31)) * kPadK + (lane >> 5) * 8;
+    bf16x8_t af[2][I], bfr[2][J];
+    auto load_frags = [&](int kk, int slot) {
+#pragma unroll
+      for (int i = 0; i < I; ++i) af[slot][i] = *(const bf16x8_t*)(Ab + i * 32 * kPadK + kk * 16);
+#pragma unroll
+      for (int j = 0; j < J; ++j) bfr[slot][j] = *(const bf16x8_t*)(Bb + j * 32 * kPadK + kk * 16);
+    };
+    auto mfmas = [&](int slot) {
+#pragma unroll
+      for (int i = 0; i < I; ++i)
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[slot][i], bfr[slot][j], acc[i][j],
+                                                              0, 0, 0);
+    };
+    load_frags(0, 0);
+    // k slice 0: write the x part of step s+1, then load the x part of step s+2
+    load_frags(1, 1);
+    mfmas(0);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (NEXT) store_a(buf ^ 1);
+    if constexpr (NEXT2) load_a(k2);
+    __builtin_amdgcn_sched_barrier(0);
+    // k slice 1: write the w part of step s+1, load half of the w part of step s+2
+    load_frags(2, 0);
+    mfmas(1);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (NEXT) store_b(buf ^ 1);
+    if constexpr (NEXT2) load_b(k2, 0, BP / 2);
+    __builtin_amdgcn_sched_barrier(0);
+    // k slice 2: the other half of the w loads
+    load_frags(3, 1);
+    mfmas(0);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (NEXT2) load_b(k2, BP / 2, BP);
+    __builtin_amdgcn_sched_barrier(0);
+    // k slice 3
+    mfmas(1);
+    __syncthreads();
+  };
+  using yes = std::true_type;
+  using no = std::false_type;
+  int s = 0;
+  for (; s + 2 < steps; ++s) step(s, yes{}, yes{});
+  if (s + 1 < steps) step(s++, yes{}, no{});
+  step(s, no{}, no{});
 
   // epilogue: fp32 -> bf16 (round to nearest even), rows past the tile end skipped
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < I; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < J; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int row = wm * 64 + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+        const int row = wm * WR + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
         const int col = n0 + wn * 64 + j * 32 + (lane & 31);
         if (row < nrows)
           y[(int64_t)(r0 + row) * Nout + col] = __builtin_bit_cast(uint16_t, (__bf16)acc[i][j][v]);
@@ -196,9 +297,13 @@ hipError_t launch_grouped_gemm(const uint16_t* x, const uint16_t* w, int32_t K, 
                                const int32_t* tile_rows, int32_t max_tiles, uint16_t* y,
                                hipStream_t stream) {
   if (max_tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL(grouped_gemm_kernel, dim3((unsigned)(max_tiles * (Nout / kBN))), dim3(256), 0,
-                     stream, x, w,
-                     K, Nout, tile_expert, tile_row0, tile_rows, y);
+  if (Nout % 256 == 0) {
+    hipLaunchKernelGGL((grouped_gemm_kernel<kBM, 256>), dim3((unsigned)(max_tiles * (Nout / 256))),
+                       dim3(512), 0, stream, x, w, K, Nout, tile_expert, tile_row0, tile_rows, y);
+  } else {
+    hipLaunchKernelGGL((grouped_gemm_kernel<kBM, 128>), dim3((unsigned)(max_tiles * (Nout / 128))),
+                       dim3(256), 0, stream, x, w, K, Nout, tile_expert, tile_row0, tile_rows, y);
+  }
   return hipGetLastError();
 }
 

@@ -348,7 +348,8 @@ moe_status moe_grouped_gemm_tiles(const int32_t* expert_offset, const int32_t* e
  *   tiles from moe_grouped_gemm_tiles with tile_m = MOE_GEMM_TILE_M,
  *   y  bf16 [rows, Nout]; rows outside every tile are not written.
  * Errors: MOE_ERR_INVALID_ARGUMENT (null or misaligned pointers, sizes < 1),
- * MOE_ERR_UNSUPPORTED (K % 64 != 0, Nout % 128 != 0, max_tiles * Nout / 128 > 2^23),
+ * MOE_ERR_UNSUPPORTED (K % 64 != 0, Nout % 128 != 0, K * 512 > 2^31 - 1,
+ * max_tiles * Nout / 128 > 2^23),
  * MOE_ERR_LAUNCH.  The tile arrays are trusted: every tile's rows must lie in [0, rows).
  */
 moe_status moe_grouped_gemm(const uint16_t* x, int64_t rows, int32_t K, const uint16_t* w,

@@ -82,8 +82,9 @@ def test_grouped_gemm_reduced(gpu_lib, cfg, M, K, Nout):
 
 
 def test_grouped_gemm_edges(gpu_lib):
-    """Experts with 0, 1, 127, 128, 129 and 300 rows; K = 64, Nout = 128."""
-    counts = [0, 1, 127, 128, 129, 300, 0, 5]
+    """Experts whose row counts sit at and around the 32-row MFMA blocks and the row
+    tile (0, 1, 5, 33, 96, 97, 127 ... 300); K = 64 and 192, Nout = 128 and 256."""
+    counts = [0, 1, 127, 128, 129, 300, 0, 5, 255, 256, 257, 33, 96, 97]
     G = len(counts)
     idx = np.concatenate([np.full(c, e, np.int32) for e, c in enumerate(counts)]).reshape(-1, 1)
     rng = np.random.default_rng(1)
