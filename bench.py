@@ -43,6 +43,7 @@ TRAFFIC_FILE = os.path.join(PROFILES, "hbm_traffic_zipf1.2-top8-M16384.txt")
 KERNEL_SOURCES = {
     "dispatch": "combine_dispatch_layout_amd/csrc/dispatch.hip",
     "combine": "combine_dispatch_layout_amd/csrc/combine.hip",
+    "grouped_gemm": "combine_dispatch_layout_amd/csrc/gemm.hip",
 }
 
 
@@ -70,13 +71,13 @@ def source_hash(rel: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def recorded_traffic(kernel: str, workload: str):
+def recorded_traffic(kernel: str, workload: str, path: str = TRAFFIC_FILE):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
     taken on the current kernel source (else None)."""
-    if not os.path.exists(TRAFFIC_FILE):
+    if not os.path.exists(path):
         return None
     vals = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
@@ -309,16 +310,28 @@ def bench_gemm(args, w, dev):
     ys = torch.empty((Ms, Ns), dtype=torch.int16, device=dev)
     s_tiles, s_gemm = _time_gemm(moedl, torch, xs, ws, ts, ys, offd, cntd, args.steps, args.warmup)
 
+    # a 2 GiB plain copy: calibrates the HBM byte counters of a profiled run of this leg
+    from combine_dispatch_layout_amd import harness
+    src = torch.empty(1 << 30, dtype=torch.int16, device=dev)
+    dst = torch.empty_like(src)
+    harness.copy(src, dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+    wl_name = f"{w.name}-grouped-gemm-K{N}-N{Nout}"
+    traffic = recorded_traffic("grouped_gemm", wl_name,
+                               os.path.join(PROFILES, f"hbm_traffic_{wl_name}.txt"))
     res = {"metric": "grouped GEMM TFLOP/s over the per-expert layout (bf16 in/out, fp32 acc)",
            "value": round(tflops, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round((t_tiles + t_gemm) * 1e-3, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic",
-           "config": {"workload": w.name + "-grouped-gemm", "rows": M * k, "K": N, "Nout": Nout,
-                      "G": G},
+           "config": {"workload": wl_name, "rows": M * k, "K": N, "Nout": Nout, "G": G},
            "roofline": {"bound": "mfma", "achieved": round(tflops, 1),
                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                        "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
+                        "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+                        "min_hbm_bytes_per_launch": int(G * Nout * N * 2 + M * k * N * 2
+                                                        + M * k * Nout * 2)},
            "event_us": {"grouped_gemm_tiles": round(t_tiles, 2), "grouped_gemm": round(t_gemm, 2)},
            "deepspeed_page_shape": {"experts": Gs, "tokens": Ms, "K": Ks, "Nout": Ns,
                                     "tiles_us": round(s_tiles, 2), "gemm_us": round(s_gemm, 2),
