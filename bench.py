@@ -91,18 +91,30 @@ def recorded_traffic(kernel: str, workload: str, path: str = TRAFFIC_FILE):
         return None
 
 
-def cpu_baseline(w, dedup: bool, alg_bytes: float):
-    """The oracle as it stands, single-threaded, on the same inputs."""
+def cpu_baseline(w, dedup: bool, max_tokens: int = 16384):
+    """The oracle as it stands, single-threaded, on the same inputs: layout, dispatch
+    and combine on the first min(M, max_tokens) tokens (the whole workload up to 16384
+    tokens), each phase timed; the stand-in expert step between dispatch and combine
+    runs but, as on the GPU, is not counted."""
     import oracle
+    Ms = min(w.M, max_tokens)
+    idx, x, wts = w.topk_idx[:Ms], w.x[:Ms], w.weights[:Ms]
+    xs = w.x_scale[:Ms] if w.x_scale is not None else None
     t0 = time.perf_counter()
-    lay = oracle.dispatch_layout(w.topk_idx, w.expert_bucket, w.B, dedup)
-    sent, _ = oracle.dispatch(w.x, lay.send_row, lay.R)
-    if dedup:
-        eo = oracle.expert_outputs("identity", sent, lay.send_row, lay.slot, w.topk_idx)
+    lay = oracle.dispatch_layout(idx, w.expert_bucket, w.B, dedup)
+    t1 = time.perf_counter()
+    sent, sent_scale = oracle.dispatch(x, lay.send_row, lay.R, xs)
+    t2 = time.perf_counter()
+    if w.standin == "identity" and not dedup and w.dtype == "bf16":
+        eo = sent                                   # combine reads the dispatched rows
     else:
-        eo = sent
-    oracle.combine(eo, w.weights, lay.slot)
-    dt = time.perf_counter() - t0
+        eo = oracle.expert_outputs(w.standin, sent, lay.send_row, lay.slot, idx, sent_scale)
+    t3 = time.perf_counter()
+    oracle.combine(eo, wts, lay.slot)
+    t4 = time.perf_counter()
+    dt = (t1 - t0) + (t2 - t1) + (t4 - t3)
+    scale_bytes = xs.shape[1] * 4 if xs is not None else 0
+    alg = (Ms + lay.R) * (w.row_bytes + scale_bytes) + (Ms * w.k + Ms) * w.N * 2
     cpu_model = "unknown"
     try:
         for line in open("/proc/cpuinfo"):
@@ -112,12 +124,13 @@ def cpu_baseline(w, dedup: bool, alg_bytes: float):
     except OSError:
         pass
     return {
-        "value": round(alg_bytes / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
-        "kind": "oracle",
-        "sample": (f"whole workload ({w.M} tokens), one pass of layout+dispatch+combine "
-                   f"({'dedup, identity expansion included' if dedup else 'combine reads the dispatched rows'}), "
-                   f"{dt:.2f} s on 1 of {len(os.sched_getaffinity(0))} host cores ({cpu_model})"),
+        "value": round(alg / dt / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "sample": (f"{'whole workload' if Ms == w.M else 'first'} {Ms} tokens, one pass of "
+                   f"layout+dispatch+combine ({dt:.2f} s; stand-in expert step excluded), "
+                   f"1 of {len(os.sched_getaffinity(0))} host cores ({cpu_model})"),
         "seconds": round(dt, 3),
+        "phase_seconds": {"layout": round(t1 - t0, 3), "dispatch": round(t2 - t1, 3),
+                          "combine": round(t4 - t3, 3)},
     }
 
 
@@ -453,35 +466,45 @@ def main():
 
     M, N, G, k, B = w.M, w.N, w.G, w.k, w.B
     row_bytes = w.row_bytes
+    fp8 = w.dtype == "fp8"
 
     idx = torch.from_numpy(w.topk_idx).to(dev)
     ebkt = torch.from_numpy(w.expert_bucket).to(dev)
-    x = torch.from_numpy(w.x.view(np.int16)).to(dev)
+    x = torch.from_numpy(w.x if fp8 else w.x.view(np.int16)).to(dev)
+    xs = torch.from_numpy(w.x_scale).to(dev) if w.x_scale is not None else None
     wts = torch.from_numpy(w.weights).to(dev)
     lay = moedl.alloc_layout(M, k, G, B, dedup, dev)
     cap = lay.capacity
-    out = torch.empty((cap, N), dtype=torch.int16, device=dev)
+    out = torch.empty((cap, N), dtype=x.dtype, device=dev)
+    out_scale = (torch.empty((cap, xs.shape[1]), dtype=torch.float32, device=dev)
+                 if xs is not None else None)
     y = torch.empty((M, N), dtype=torch.int16, device=dev)
-    eo = out if not dedup else torch.empty((M * k, N), dtype=torch.int16, device=dev)
+    # identity experts without dedup: combine reads the dispatched rows in place;
+    # otherwise the stand-in expert step (untimed) writes slot-indexed bf16 outputs
+    in_place = w.standin == "identity" and not dedup and not fp8
+    eo = out if in_place else torch.empty((M * k, N), dtype=torch.int16, device=dev)
     slot_eo = lay.slot
 
     def step():
         moedl.moe_dispatch_layout(idx, ebkt, B, dedup, out=lay)
-        moedl.moe_dispatch(x, lay.send_row, cap, out=out, dedup=dedup)
+        moedl.moe_dispatch(x, lay.send_row, cap, x_scale=xs, out=out, out_scale=out_scale,
+                           dedup=dedup)
         moedl.moe_combine(eo, wts, slot_eo, y=y)
 
-    # warm-up (and one untimed dedup expansion so combine has real inputs)
+    # warm-up (and one untimed expert step so combine has real inputs)
     for _ in range(max(1, args.warmup)):
         step()
-    if dedup:
-        harness.expert_outputs("identity", out, lay.send_row, lay.slot, idx, out=eo)
+    if not in_place:
+        harness.expert_outputs(w.standin, out, lay.send_row, lay.slot, idx, out_scale, out=eo)
     torch.cuda.synchronize()
     R = int(lay.bucket_offset[B].item())
     assert int(lay.status.item()) == 0
 
-    # algorithmic bytes: read x once, write R send rows, read M*k expert rows, write M rows
-    disp_bytes = (M + R) * row_bytes
-    comb_bytes = (M * k + M) * row_bytes
+    # algorithmic bytes: read x (and scales) once, write R send rows (and scales), read
+    # M*k bf16 expert rows, write M bf16 rows
+    scale_bytes = xs.shape[1] * 4 if xs is not None else 0
+    disp_bytes = (M + R) * (row_bytes + scale_bytes)
+    comb_bytes = (M * k + M) * N * 2
     total_bytes = disp_bytes + comb_bytes
 
     # ---- timed region: exactly `steps` steps, per-kernel HIP events on the same stream
@@ -495,7 +518,8 @@ def main():
         e[0].record(stream)
         moedl.moe_dispatch_layout(idx, ebkt, B, dedup, out=lay)
         e[1].record(stream)
-        moedl.moe_dispatch(x, lay.send_row, cap, out=out, dedup=dedup)
+        moedl.moe_dispatch(x, lay.send_row, cap, x_scale=xs, out=out, out_scale=out_scale,
+                           dedup=dedup)
         e[2].record(stream)
         moedl.moe_combine(eo, wts, slot_eo, y=y)
         e[3].record(stream)
@@ -548,12 +572,39 @@ def main():
     ce.record()
     torch.cuda.synchronize()
     copy_gbps = 2 * nbytes * 10 / (cs.elapsed_time(ce) * 1e-3) / 1e9
+    dst.copy_(src)                      # device-to-device memcpy of the same 2 GiB
+    torch.cuda.synchronize()
+    cs.record()
+    for _ in range(10):
+        dst.copy_(src)
+    ce.record()
+    torch.cuda.synchronize()
+    memcpy_gbps = 2 * nbytes * 10 / (cs.elapsed_time(ce) * 1e-3) / 1e9
     del src, dst
 
-    # correctness guard on the timed buffers (identity experts: y == x)
+    # correctness guard on the timed buffers, closed forms of the stand-in experts
+    # (weights of a token sum to one): identity y == x exactly; scaled experts
+    # y ~ x * sum_j w_j (1 + e_j / 256) within two bf16 roundings; fp8 experts
+    # y ~ dequant(x) * sum_j w_j within one rounding (sampled tokens)
     torch.cuda.synchronize()
-    xz = torch.where(x == -32768, torch.zeros_like(x), x)
-    assert bool((y == xz).all().item()), "combine output differs from the input rows"
+    if w.standin == "identity":
+        xz = torch.where(x == -32768, torch.zeros_like(x), x)
+        assert bool((y == xz).all().item()), "combine output differs from the input rows"
+    else:
+        ts = torch.arange(0, M, 61, device=dev)
+        wt = wts[ts].double()
+        if w.standin == "scale":
+            f = (wt * (1.0 + idx[ts].double() / 256.0)).sum(1, keepdim=True)
+            ref = x[ts].view(torch.bfloat16).double() * f
+            tol = 2.0 ** -7
+        else:
+            q = x[ts].cpu().view(torch.float8_e4m3fn).double()
+            sc = xs[ts].cpu().double().repeat_interleave(128, dim=1)
+            ref = (q * sc).to(dev) * wt.sum(1, keepdim=True)
+            tol = 2.0 ** -8 * 1.001
+        got = y[ts].view(torch.bfloat16).double()
+        assert bool(((got - ref).abs() <= ref.abs() * tol + 1e-30).all().item()), \
+            f"combine output off the {w.standin} closed form"
 
     # ---- roofline of the dominant kernel
     kernels = {"dispatch": (disp_ms, disp_bytes), "combine": (comb_ms, comb_bytes)}
@@ -568,16 +619,16 @@ def main():
 
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(w, dedup, total_bytes)
+        cpu = cpu_baseline(w, dedup, 16384 if in_place else 8192)
 
     res = {
         "metric": METRIC, "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if not fp8 else "fp8_e4m3 rows, bf16 combine", "data": "synthetic",
         "config": {"workload": w.name + ("-dedup" if dedup else ""), "M": M, "N": N, "G": G,
-                   "k": k, "B": B, "routing": "zipf(1.2) top-8 without replacement",
-                   "dedup": dedup, "send_rows": R, "parallelism": "single-gpu"},
+                   "k": k, "B": B, "dtype": w.dtype, "experts": w.standin, "dedup": dedup,
+                   "send_rows": R, "parallelism": "single-gpu"},
         "us_per_step": round(ms_per_step * 1e3, 2),
         "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
         "alg_bytes_per_step": total_bytes,
@@ -587,6 +638,7 @@ def main():
         "graph_replay_us_per_step": None if graph_us is None else round(graph_us, 2),
         "graph_replay_gbps": None if graph_us is None else round(total_bytes / (graph_us * 1e-6) / 1e9, 1),
         "copy_ceiling_gbps": round(copy_gbps, 1),
+        "memcpy_dtod_gbps": round(memcpy_gbps, 1),
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -25,8 +25,8 @@
 // Scales (fp8 rows): the workgroup of piece 0 copies each destination's
 // N/128-float scale row beside the data.
 //
-// With a dedup layout (the caller says so) a second shape is used, below.  Both
-// shapes write the same bytes.
+// With a dedup layout (the caller says so), or a send buffer above 3 GiB, a second
+// shape is used, below.  Both shapes write the same bytes.
 #include "moe_internal.h"
 
 namespace moedl {
@@ -51,13 +51,19 @@ __global__ __launch_bounds__(64 * MOE_MAX_TOPK) void dispatch_piece_kernel(
   if (skip) return;
 
   const int c = piece * kPieceVecs + lane;
+  // the first 64 scales of the row are loaded together with the data, so the wave
+  // waits for one round trip, not two
+  const bool scales = x_scale != nullptr && piece == 0;
+  float s0 = 0.0f;
+  if (scales && lane < scale_cols) s0 = x_scale[t * scale_cols + lane];
   if (c < row_vecs) {
     const u32x4 v = x[t * row_vecs + c];
     __builtin_nontemporal_store(v, out + (int64_t)r * row_vecs + c);
   }
-  if (x_scale != nullptr && piece == 0) {
-    for (int sc = lane; sc < scale_cols; sc += 64)
-      out_scale[(int64_t)r * scale_cols + sc] = x_scale[t * scale_cols + sc];
+  if (scales) {
+    if (lane < scale_cols) __builtin_nontemporal_store(s0, out_scale + (int64_t)r * scale_cols + lane);
+    for (int sc = lane + 64; sc < scale_cols; sc += 64)
+      __builtin_nontemporal_store(x_scale[t * scale_cols + sc], out_scale + (int64_t)r * scale_cols + sc);
   }
 }
 
@@ -122,7 +128,13 @@ hipError_t launch_dispatch(const void* x, int64_t M, int64_t row_bytes, const fl
   const int32_t pieces = (row_vecs + kPieceVecs - 1) / kPieceVecs;
   const int64_t blocks = M * pieces;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  if (dedup) {
+  // The k single-store waves shape is the faster one for send buffers up to ~2 GB
+  // (Zipf, 16384 tokens x 14 KiB x 8: 6.4 vs 6.0 TB/s), but with a send buffer of
+  // ~3.8 GB or more (65536 tokens x 8 x 7 KiB, or x 14 KiB) it falls to ~3.6 TB/s while
+  // the shape of two waves sharing a token's rows holds ~5.3 TB/s (measured on MI355X,
+  // with and without scales, fp8 and bf16 alike).  So large buffers take that shape too.
+  constexpr int64_t kSharedShapeBytes = (int64_t)3 << 30;
+  if (dedup || out_rows * row_bytes > kSharedShapeBytes) {
 #define MOEDL_CASE(K)                                                                          \
   case K:                                                                                      \
     return launch_dedup_k<K>(x, M, row_vecs, pieces, x_scale, scale_cols, send_row, out,     \

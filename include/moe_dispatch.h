@@ -139,7 +139,8 @@ moe_status moe_dispatch_layout(const int32_t* topk_idx, int64_t M, int32_t k,
  *   send_row  int32 [M*k] from moe_dispatch_layout (any map into rows works).
  *   dedup     0 or 1: whether send_row came from a dedup layout.  Only selects the
  *             kernel shape (k single-store waves per row piece, or two waves sharing
- *             the token's distinct rows); the bytes written are the same.
+ *             the token's distinct rows; the latter also for send buffers above
+ *             3 GiB); the bytes written are the same.
  * Outputs:
  *   out       [out_rows, N] elements of `dtype`; rows named by send_row are written.
  *   out_scale float [out_rows, N/128]; NULL exactly when x_scale is NULL.
@@ -348,7 +349,7 @@ moe_status moe_grouped_gemm_tiles(const int32_t* expert_offset, const int32_t* e
  *   tiles from moe_grouped_gemm_tiles with tile_m = MOE_GEMM_TILE_M,
  *   y  bf16 [rows, Nout]; rows outside every tile are not written.
  * Errors: MOE_ERR_INVALID_ARGUMENT (null or misaligned pointers, sizes < 1),
- * MOE_ERR_UNSUPPORTED (K % 64 != 0, Nout % 128 != 0, K * 512 > 2^31 - 1,
+ * MOE_ERR_UNSUPPORTED (K % 64 != 0, Nout % 128 != 0, MOE_GEMM_TILE_M * K * 2 > 2^31 - 1,
  * max_tiles * Nout / 128 > 2^23),
  * MOE_ERR_LAUNCH.  The tile arrays are trusted: every tile's rows must lie in [0, rows).
  */
