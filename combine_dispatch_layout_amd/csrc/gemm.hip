@@ -13,20 +13,13 @@
 // in ascending id, tile_m rows each, the last shorter); unused entries of the tile
 // arrays get expert -1 so a GEMM grid sized by the host-side bound simply exits there.
 //
-// grouped_gemm_kernel: one 256-thread workgroup per (row tile, column block of 256, or of
-// 128 when Nout is not a multiple of 256).
-//  - Grid: one linear index over max_tiles * Nout / BN workgroups, row tile major.
-//  - Both operands are K-contiguous ([rows, K] and [Nout, K]), which is what an MFMA
-//    lane needs: 8 consecutive k of one row / one column.
-//  - Per 64-wide k step the workgroup stages the tile's 128 x 64 x values and BN x 64
-//    weights in one of two LDS buffers (rows padded to 72 bf16 so the 16-byte fragment
-//    reads of consecutive rows hit distinct bank groups); the next step's global loads
-//    are in flight in registers meanwhile; one barrier per step.
-//  - 2 * BN / 64 waves (8 for BN = 256) form a 2 x BN/64 grid of 64 x 64 output blocks;
-//    each wave runs 2 x 2 v_mfma_f32_32x32x16_bf16 per 16-wide k slice.  Accumulator lane layout
-//    (verified on the GPU): value v of lane l is C[8*(v/4) + 4*(l/32) + v%4][l%32];
-//    operand lane l holds A[l%32][8*(l/32) + i] and B[8*(l/32) + i][l%32].
-//  - Rows past the tile's end read as zero and are not stored.
+// grouped_gemm_kernel: one workgroup per (128-row tile, column block of 256, or of 128
+// when Nout is not a multiple of 256), details at the kernel.  Both operands are
+// K-contiguous ([rows, K] and [Nout, K]), which is what an MFMA lane needs: 8
+// consecutive k of one row or one column.  Accumulator lane layout of
+// v_mfma_f32_32x32x16_bf16 (verified on the GPU): value v of lane l is
+// C[8*(v/4) + 4*(l/32) + v%4][l%32]; operand lane l holds A[l%32][8*(l/32) + i] and
+// B[8*(l/32) + i][l%32].
 #include <type_traits>
 
 #include "moe_internal.h"
@@ -98,27 +91,29 @@ __device__ __forceinline__ void gemm_block_order(int bid, int nblk, int* tile, i
   *jblk = bid - *tile * nblk;
 }
 
-// One workgroup = one BM-row tile (BM = 256) x BN columns (BN = 256, or 128 when Nout is
-// not a multiple of 256), 2 * BN / 64 waves: wave (wm, wn) owns the BM/2 x 64 output
-// block at rows wm*BM/2, columns wn*64, i.e. BM/64 x 2 accumulator blocks of 32 x 32.
-// With BN = 256 that is 8 waves, two per SIMD.
-// A 256 x 256 tile moves (256 + 256) * 64 * 2 bytes per 64-wide k step for 2 * 256 *
-// 256 * 64 flops, a third fewer bytes per flop than 128 x 256: the global -> LDS path
-// bounds this kernel, not the matrix cores (measured: without the per-step loads and
-// LDS writes it runs at ~1.97 PFLOP/s).
+// One workgroup = one BM-row tile (BM = 128) x BN columns, 2 * BN / 64 waves: wave
+// (wm, wn) owns the BM/2 x 64 output block at rows wm*BM/2, columns wn*64, i.e. 2 x 2
+// accumulator blocks of 32 x 32.  With BN = 256 that is 8 waves, two per SIMD.
+// What bounds it (measured): without the per-step global loads and LDS writes the same
+// kernel runs at ~1.97 PFLOP/s, so the global -> register -> LDS staging path, not the
+// matrix cores, sets the rate.  A 256 x 256 tile needs a third fewer bytes per flop and
+// wins on a uniform layout (1.22 vs 1.08 PFLOP/s), but loses on the Zipf layout, whose
+// many short expert tiles pay full weight loads.
 // Short tiles (an expert's last rows): x is read through a buffer resource whose size
 // ends at the tile's last row, so rows past the end come back as zeros with no memory
 // traffic and every load stays unconditional.  (Skipping the MFMAs of 32-row blocks
 // past the end was measured slower: the branch splits the MFMA / load interleave.)
-// Per 64-wide k step s: the MFMAs read LDS buffer s%2 (fragments double-buffered in
-// registers across the four 16-wide k slices) while the tile of step s+1, loaded into
-// registers during step s-1, is written to buffer (s+1)%2 and the tile of step s+2 is
-// loaded.  A wave issues in order, so those LDS writes and global loads are placed
-// between the MFMA groups of the k slices (sched_barrier fences keep them there): the
-// address unit then works while the matrix cores do.  Issued after all of a step's
-// MFMAs instead, they form one burst per step that the matrix cores wait through.  The
-// loop body has no branches (the last two steps are peeled), which keeps the compiler's
-// memory wait counts exact.  One barrier per step orders the two LDS buffers.
+// Per 64-wide k step s: the MFMAs read LDS buffer s%2 (rows padded to 72 bf16: the
+// 16-byte fragment reads of consecutive rows hit distinct bank groups; fragments are
+// double-buffered in registers across the four 16-wide k slices) while the tile of step
+// s+1, loaded into registers during step s-1, is written to buffer (s+1)%2 and the tile
+// of step s+2 is loaded.  A wave issues in order, so those LDS writes and global loads
+// are placed between the MFMA groups of the k slices (sched_barrier fences keep them
+// there): the address unit then works while the matrix cores do.  Issued after all of
+// a step's MFMAs instead, they form one burst per step that the matrix cores wait
+// through.  The loop body has no branches (the last two steps are peeled), which keeps
+// the compiler's memory wait counts exact.  One barrier per step orders the two LDS
+// buffers.
 template <int BM, int BN>
 __global__ __launch_bounds__(2 * BN) void grouped_gemm_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wgt, int32_t K, int32_t Nout,
