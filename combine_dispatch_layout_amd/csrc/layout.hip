@@ -304,7 +304,8 @@ struct OrderLds {
 
 // Offsets of expert runs laid out in (bucket, id) order, from per-expert counts
 // cnt[G] (LDS).  NT-thread workgroup; wave w handles a contiguous range of experts so
-// the cross-wave prefix keeps id order.  Writes offset[e] (global or LDS).
+// the cross-wave prefix keeps id order.  A map whose bucket never decreases with the
+// id takes a fast path (id order).  Writes offset[e] (global or LDS).
 template <int NT>
 __device__ void expert_order_offsets(OrderLds<NT>& lds, const unsigned char* map_s,
                                      const int32_t* cnt, int32_t G, int32_t B,
@@ -315,6 +316,31 @@ __device__ void expert_order_offsets(OrderLds<NT>& lds, const unsigned char* map
   const int lane = tid & 63;
   const int w = wave_index();
   const int per = ((G + NW - 1) / NW + 63) / 64 * 64;  // experts per wave, whole chunks
+
+  // Contiguous maps (the bucket never decreases with the expert id; the common case)
+  // order experts by id: the ranking is skipped and the counts are scanned in place.
+  int mono = 1;
+  for (int e = tid; e + 1 < G; e += NT) mono &= map_s[e] <= map_s[e + 1];
+  if (__syncthreads_and(mono)) {
+    int local[CH];
+    int sum = 0;
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const int i = tid * CH + u;
+      local[u] = i < G ? cnt[i] : 0;
+      sum += local[u];
+    }
+    int run = block_exclusive_scan<NT>(sum, lds.wave_sums);
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const int i = tid * CH + u;
+      if (i < G) offset[i] = run;
+      run += local[u];
+    }
+    __syncthreads();
+    return;
+  }
+
   for (int i = tid; i < NW * kMaxB; i += NT) lds.wbc[i / kMaxB][i % kMaxB] = 0;
   __syncthreads();
 
