@@ -30,6 +30,7 @@ import json
 import os
 import sys
 import time
+from typing import Optional
 
 import numpy as np
 
@@ -39,7 +40,6 @@ sys.path.insert(0, ROOT)
 METRIC = "dispatch+combine µs and HBM GB/s (% of peak), M=16384,N=7168,G=256,k=8"
 HBM_PEAK_GBPS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
-TRAFFIC_FILE = os.path.join(PROFILES, "hbm_traffic_zipf1.2-top8-M16384.txt")
 KERNEL_SOURCES = {
     "dispatch": "combine_dispatch_layout_amd/csrc/dispatch.hip",
     "combine": "combine_dispatch_layout_amd/csrc/combine.hip",
@@ -71,9 +71,10 @@ def source_hash(rel: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def recorded_traffic(kernel: str, workload: str, path: str = TRAFFIC_FILE):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
-    taken on the current kernel source (else None)."""
+def recorded_traffic(kernel: str, workload: str, path: Optional[str] = None):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of this
+    workload, if it was taken on the current kernel source (else None)."""
+    path = path or os.path.join(PROFILES, f"hbm_traffic_{workload}.txt")
     if not os.path.exists(path):
         return None
     vals = {}
