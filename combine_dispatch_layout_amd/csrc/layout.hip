@@ -11,19 +11,22 @@
 //    routing-pattern expert placement ...", the copy-reduction item).
 //
 // Building blocks (device functions shared by the kernels below):
-//  - tile_expert_ranks: one 256-thread workgroup, 256 tokens.  Each wave64 walks its
-//    64 tokens' k*64 (t, j) entries in flat order, 64 at a time.  Entries of one
-//    64-entry chunk that name the same expert are found with ceil(log2 G) ballots
-//    (lanes agreeing on every bit of the id); one leader lane per distinct expert
-//    bumps the wave's LDS counter, so there are no same-address LDS atomics under
-//    skew.  The lane's rank among its peers (mbcnt) plus the counter's old value is
-//    the entry's stable rank in the wave; a cross-wave prefix makes it the rank in the
-//    tile.
+//  - tile_expert_ranks: one 256-thread workgroup, 256 tokens.  Each wave64 holds NC
+//    consecutive 64-entry chunks of the tile's (t, j) entries in flat order.  Entries
+//    of a chunk that name the same expert are found with ceil(log2 G) ballots (lanes
+//    agreeing on every bit of the id), the ballots of all chunks interleaved; per
+//    chunk, one leader lane per distinct expert adds the chunk's count to the wave's
+//    LDS counter with an atomic that returns the old value (a wave's LDS operations
+//    complete in order, so it counts the earlier chunks), and the peers fetch it from
+//    the leader.  No same-address LDS atomics under skew.  That value plus the lane's
+//    rank among its peers (mbcnt) is the entry's stable rank in the wave; a cross-wave
+//    prefix makes it the rank in the tile.
 //  - tile_dedup_ranks: token view (lane = token).  Per-token bucket bitmask; one
 //    ballot per bucket gives each token's rank among the tile's tokens sending there.
 //  - expert_order_offsets: experts ranked by (bucket, id) with the same ballot
 //    matching (key = bucket), then a block-wide exclusive scan of the counts in that
-//    order gives every expert's offset.
+//    order gives every expert's offset; a map whose bucket never decreases with the
+//    id skips the ranking (id order).
 //
 // Kernels:
 //  - M <= 256 tokens (one tile): layout_single_kernel does everything in LDS in one
