@@ -237,24 +237,27 @@ __device__ __forceinline__ void tile_dedup_ranks(TileLds<KC>& lds, int32_t M, in
   const int64_t t = (int64_t)tile * kTileTokens + (int64_t)w * 64 + lane;
   const bool tv = t < M;
   const int* my_ids = lds.ids_s + (w * 64 + lane) * k;
+  // Branch-free throughout: every LDS read is unconditional (clamped index, value
+  // replaced afterwards), so the reads of all j are in flight together.
+  int ev[KC];
+#pragma unroll
+  for (int j = 0; j < KC; ++j) ev[j] = (j < k && tv) ? my_ids[j] : kAbsent;
   uint64_t bmask = 0;
 #pragma unroll
   for (int j = 0; j < KC; ++j) {
-    eb[j] = kBadBucket;
-    if (j < k && tv) {
-      const int e = my_ids[j];
-      if (e >= 0) {
-        eb[j] = lds.map_s[e];
-        if (eb[j] != kBadBucket) bmask |= 1ull << eb[j];
-      }
-    }
+    const int m = lds.map_s[ev[j] >= 0 ? ev[j] : 0];
+    eb[j] = ev[j] >= 0 ? m : kBadBucket;
+    if (eb[j] != kBadBucket) bmask |= 1ull << eb[j];
   }
+  // one ballot per bucket; lane b keeps bucket b's ballot and writes it
+  uint64_t mine = 0;
   for (int b = 0; b < B; ++b) {
     const uint64_t bal = wave_ballot(tv && ((bmask >> b) & 1ull));
-    if (lane == 0) {
-      lds.wbal[w][b] = bal;
-      lds.wbcnt[w][b] = __builtin_popcountll(bal);
-    }
+    mine = lane == b ? bal : mine;
+  }
+  if (lane < B) {
+    lds.wbal[w][lane] = mine;
+    lds.wbcnt[w][lane] = __builtin_popcountll(mine);
   }
   __syncthreads();
   if (tid < B) {
@@ -270,9 +273,10 @@ __device__ __forceinline__ void tile_dedup_ranks(TileLds<KC>& lds, int32_t M, in
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < KC; ++j) {
-    const int b = eb[j];
-    dl[j] = b != kBadBucket ? lds.wbcnt[w][b] + __builtin_popcountll(lds.wbal[w][b] & below)
-                            : -1;
+    const int b = eb[j] != kBadBucket ? eb[j] : 0;
+    const int base = lds.wbcnt[w][b];
+    const uint64_t bal = lds.wbal[w][b];
+    dl[j] = eb[j] != kBadBucket ? base + __builtin_popcountll(bal & below) : -1;
   }
 }
 
