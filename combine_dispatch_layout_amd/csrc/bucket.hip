@@ -33,14 +33,6 @@ namespace {
 
 constexpr int kPieceVecs = 64;
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const f32x2_t f = {lo, hi};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
-}
-
 __device__ __forceinline__ void accumulate(float (&acc)[8], const u32x4 v, const float wj) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {

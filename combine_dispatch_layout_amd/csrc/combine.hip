@@ -30,14 +30,6 @@ namespace {
 
 constexpr int kPieceVecs = 64;
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const f32x2_t f = {lo, hi};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
-}
-
 template <int K, int NW>
 __global__ __launch_bounds__(64 * NW) void combine_piece_kernel(
     const u32x4* __restrict__ eo, int64_t expert_rows, const float* __restrict__ wts,
