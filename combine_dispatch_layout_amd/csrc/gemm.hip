@@ -94,11 +94,13 @@ __device__ __forceinline__ void gemm_block_order(int bid, int nblk, int* tile, i
 // One workgroup = one BM-row tile (BM = 128) x BN columns, 2 * BN / 64 waves: wave
 // (wm, wn) owns the BM/2 x 64 output block at rows wm*BM/2, columns wn*64, i.e. 2 x 2
 // accumulator blocks of 32 x 32.  With BN = 256 that is 8 waves, two per SIMD.
-// What bounds it (measured): without the per-step global loads and LDS writes the same
-// kernel runs at ~1.97 PFLOP/s, so the global -> register -> LDS staging path, not the
-// matrix cores, sets the rate.  A 256 x 256 tile needs a third fewer bytes per flop and
-// wins on a uniform layout (1.22 vs 1.08 PFLOP/s), but loses on the Zipf layout, whose
-// many short expert tiles pay full weight loads.
+// What bounds it (measured on the Zipf layout, random bf16): the kernel runs at ~0.87
+// PFLOP/s; with the global loads replaced by register constants (LDS writes kept) at
+// 1.38, with every load redirected to one tile so that all hit in L2 at 1.11, and with
+// the LDS writes dropped at 0.98.  So the global loads set the rate, about half through
+// the bytes each CU moves per flop and half through L2 misses to the fabric.  A 256-row
+// tile moves a third fewer bytes per flop: 1.05 vs 0.93 PFLOP/s on a uniform layout,
+// but on the Zipf layout its padding of short expert tiles eats the gain (0.88 useful).
 // Short tiles (an expert's last rows): x is read through a buffer resource whose size
 // ends at the tile's last row, so rows past the end come back as zeros with no memory
 // traffic and every load stays unconditional.  (Skipping the MFMAs of 32-row blocks
@@ -106,14 +108,16 @@ __device__ __forceinline__ void gemm_block_order(int bid, int nblk, int* tile, i
 // Per 64-wide k step s: the MFMAs read LDS buffer s%2 (rows padded to 72 bf16: the
 // 16-byte fragment reads of consecutive rows hit distinct bank groups; fragments are
 // double-buffered in registers across the four 16-wide k slices) while the tile of step
-// s+1, loaded into registers during step s-1, is written to buffer (s+1)%2 and the tile
-// of step s+2 is loaded.  A wave issues in order, so those LDS writes and global loads
-// are placed between the MFMA groups of the k slices (sched_barrier fences keep them
-// there): the address unit then works while the matrix cores do.  Issued after all of
-// a step's MFMAs instead, they form one burst per step that the matrix cores wait
-// through.  The loop body has no branches (the last two steps are peeled), which keeps
-// the compiler's memory wait counts exact.  One barrier per step orders the two LDS
-// buffers.
+// s+1, loaded into registers during step s-2, is written to buffer (s+1)%2 and the tile
+// of step s+3 is loaded into the registers it leaves: two register sets give the loads
+// two steps to arrive (2-3% faster than one step ahead, bit-identical output).  A wave
+// issues in order, so those LDS writes and global loads are placed between the MFMA
+// groups of the k slices (sched_barrier fences keep them there): the address unit then
+// works while the matrix cores do.  Issued after all of a step's MFMAs instead, they
+// form one burst per step that the matrix cores wait through.  The loop body has no
+// branches (steps run in pairs so each register set is static; the last steps are
+// peeled), which keeps the compiler's memory wait counts exact.  One barrier per step
+// orders the two LDS buffers.
 template <int BM, int BN>
 __global__ __launch_bounds__(2 * BN) void grouped_gemm_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wgt, int32_t K, int32_t Nout,
@@ -146,30 +150,32 @@ __global__ __launch_bounds__(2 * BN) void grouped_gemm_kernel(
   const uint16_t* wb = wgt + ((int64_t)e * Nout + n0) * K;
 
   // global -> register staging: thread t moves the 16-byte chunk (t % 8) of rows
-  // t / 8 + RS p; eight consecutive threads cover one row's 128 bytes
+  // t / 8 + RS p; eight consecutive threads cover one row's 128 bytes.  Two register
+  // sets: the tile of step s+1 is in set (s+1)%2 and that of step s+2 in set s%2.
   const int lrow = tid >> 3;
   const int lcol = (tid & 7) * 8;
-  u32x4 ra[AP], rb[BP];
-  auto load_a = [&](int k0) {
+  u32x4 ra[2][AP], rb[2][BP];
+  auto load_a = [&](int set, int k0) {
 #pragma unroll
     for (int p = 0; p < AP; ++p) {
       const int row = lrow + p * RS;
-      ra[p] = __builtin_bit_cast(
+      ra[set][p] = __builtin_bit_cast(
           u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, (row * K + k0 + lcol) * 2, 0, 0));
     }
   };
-  auto load_b = [&](int k0, int p0, int p1) {
+  auto load_b = [&](int set, int k0, int p0, int p1) {
 #pragma unroll
     for (int p = 0; p < BP; ++p)
-      if (p >= p0 && p < p1) rb[p] = *(const u32x4*)(wb + (int64_t)(lrow + p * RS) * K + k0 + lcol);
+      if (p >= p0 && p < p1)
+        rb[set][p] = *(const u32x4*)(wb + (int64_t)(lrow + p * RS) * K + k0 + lcol);
   };
-  auto store_a = [&](int buf) {
+  auto store_a = [&](int set, int buf) {
 #pragma unroll
-    for (int p = 0; p < AP; ++p) *(u32x4*)(&As[buf][(lrow + p * RS) * kPadK + lcol]) = ra[p];
+    for (int p = 0; p < AP; ++p) *(u32x4*)(&As[buf][(lrow + p * RS) * kPadK + lcol]) = ra[set][p];
   };
-  auto store_b = [&](int buf) {
+  auto store_b = [&](int set, int buf) {
 #pragma unroll
-    for (int p = 0; p < BP; ++p) *(u32x4*)(&Bs[buf][(lrow + p * RS) * kPadK + lcol]) = rb[p];
+    for (int p = 0; p < BP; ++p) *(u32x4*)(&Bs[buf][(lrow + p * RS) * kPadK + lcol]) = rb[set][p];
   };
 
   f32x16_t acc[I][J];
@@ -179,24 +185,29 @@ __global__ __launch_bounds__(2 * BN) void grouped_gemm_kernel(
     for (int j = 0; j < J; ++j) acc[i][j] = (f32x16_t){};
 
   const int steps = K / kBK;
-  load_a(0);
-  load_b(0, 0, BP);
-  store_a(0);
-  store_b(0);
+  load_a(0, 0);
+  load_b(0, 0, 0, BP);
   if (steps > 1) {
-    load_a(kBK);
-    load_b(kBK, 0, BP);
+    load_a(1, kBK);
+    load_b(1, kBK, 0, BP);
+  }
+  store_a(0, 0);
+  store_b(0, 0);
+  if (steps > 2) {
+    load_a(0, 2 * kBK);
+    load_b(0, 2 * kBK, 0, BP);
   }
   __syncthreads();
-  // One k step.  NEXT: the tile of step s+1 is written to the other buffer; NEXT2: the
-  // tile of step s+2 is loaded.  The steady-state loop runs with both set and no
-  // branches in its body, so the compiler's wait counts stay exact; the last two steps
-  // are peeled.
-  auto step = [&](int s, auto next_c, auto next2_c) {
+  // One k step on LDS buffer s%2.  NEXT: the tile of step s+1 (register set SET =
+  // (s+1)%2) is written to the other buffer; LOAD: the tile of step s+3 is then loaded
+  // into that set.  The loop below runs with both set and no branches in its body, so
+  // the compiler's wait counts stay exact; the last steps are peeled.
+  auto step = [&](int s, auto set_c, auto next_c, auto load_c) {
+    constexpr int SET = decltype(set_c)::value;
     constexpr bool NEXT = decltype(next_c)::value;
-    constexpr bool NEXT2 = decltype(next2_c)::value;
+    constexpr bool LOAD = decltype(load_c)::value;
     const int buf = s & 1;
-    const int k2 = (s + 2) * kBK;
+    const int k3 = (s + 3) * kBK;
     const uint16_t* Ab = As[buf] + (wm * WR + (lane & 31)) * kPadK + (lane >> 5) * 8;
     const uint16_t* Bb = Bs[buf] + (wn * 64 + (lane & 31)) * kPadK + (lane >> 5) * 8;
     bf16x8_t af[2][I], bfr[2][J];
@@ -215,25 +226,25 @@ __global__ __launch_bounds__(2 * BN) void grouped_gemm_kernel(
                                                               0, 0, 0);
     };
     load_frags(0, 0);
-    // k slice 0: write the x part of step s+1, then load the x part of step s+2
+    // k slice 0: write the x part of step s+1, then load the x part of step s+3
     load_frags(1, 1);
     mfmas(0);
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (NEXT) store_a(buf ^ 1);
-    if constexpr (NEXT2) load_a(k2);
+    if constexpr (NEXT) store_a(SET, buf ^ 1);
+    if constexpr (LOAD) load_a(SET, k3);
     __builtin_amdgcn_sched_barrier(0);
-    // k slice 1: write the w part of step s+1, load half of the w part of step s+2
+    // k slice 1: write the w part of step s+1, load half of the w part of step s+3
     load_frags(2, 0);
     mfmas(1);
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (NEXT) store_b(buf ^ 1);
-    if constexpr (NEXT2) load_b(k2, 0, BP / 2);
+    if constexpr (NEXT) store_b(SET, buf ^ 1);
+    if constexpr (LOAD) load_b(SET, k3, 0, BP / 2);
     __builtin_amdgcn_sched_barrier(0);
     // k slice 2: the other half of the w loads
     load_frags(3, 1);
     mfmas(0);
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (NEXT2) load_b(k2, BP / 2, BP);
+    if constexpr (LOAD) load_b(SET, k3, BP / 2, BP);
     __builtin_amdgcn_sched_barrier(0);
     // k slice 3
     mfmas(1);
@@ -241,10 +252,34 @@ __global__ __launch_bounds__(2 * BN) void grouped_gemm_kernel(
   };
   using yes = std::true_type;
   using no = std::false_type;
+  using set0 = std::integral_constant<int, 0>;
+  using set1 = std::integral_constant<int, 1>;
+  // pairs of steps (s even, then s + 1), so the register set of each is static
   int s = 0;
-  for (; s + 2 < steps; ++s) step(s, yes{}, yes{});
-  if (s + 1 < steps) step(s++, yes{}, no{});
-  step(s, no{}, no{});
+  for (; s + 4 < steps; s += 2) {
+    step(s, set1{}, yes{}, yes{});
+    step(s + 1, set0{}, yes{}, yes{});
+  }
+  switch (steps - s) {  // 1 to 4 steps left, s even
+    case 4:
+      step(s, set1{}, yes{}, yes{});
+      step(s + 1, set0{}, yes{}, no{});
+      step(s + 2, set1{}, yes{}, no{});
+      step(s + 3, set0{}, no{}, no{});
+      break;
+    case 3:
+      step(s, set1{}, yes{}, no{});
+      step(s + 1, set0{}, yes{}, no{});
+      step(s + 2, set1{}, no{}, no{});
+      break;
+    case 2:
+      step(s, set1{}, yes{}, no{});
+      step(s + 1, set0{}, no{}, no{});
+      break;
+    default:
+      step(s, set1{}, no{}, no{});
+      break;
+  }
 
   // epilogue: fp32 -> bf16 (round to nearest even), rows past the tile end skipped
 #pragma unroll
