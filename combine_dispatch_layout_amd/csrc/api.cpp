@@ -232,8 +232,8 @@ moe_status moe_grouped_gemm(const uint16_t* x, int64_t rows, int32_t K, const ui
   if (rows > 0 && (!x || !y)) return MOE_ERR_INVALID_ARGUMENT;
   if ((x && !aligned16(x)) || !aligned16(w)) return MOE_ERR_INVALID_ARGUMENT;
   if (rows == 0) return MOE_OK;
-  return from_hip(moedl::launch_grouped_gemm(x, w, K, Nout, tile_expert, tile_row0, tile_rows,
-                                             max_tiles, y, stream));
+  return from_hip(moedl::launch_grouped_gemm(x, rows, w, G, K, Nout, tile_expert, tile_row0,
+                                             tile_rows, max_tiles, y, stream));
 }
 
 }  // extern "C"

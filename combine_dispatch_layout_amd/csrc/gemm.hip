@@ -120,9 +120,10 @@ __device__ __forceinline__ void gemm_block_order(int bid, int nblk, int* tile, i
 // orders the two LDS buffers.
 template <int BM, int BN>
 __global__ __launch_bounds__(2 * BN) void grouped_gemm_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wgt, int32_t K, int32_t Nout,
-    const int32_t* __restrict__ tile_expert, const int32_t* __restrict__ tile_row0,
-    const int32_t* __restrict__ tile_rows, uint16_t* __restrict__ y) {
+    const uint16_t* __restrict__ x, int64_t rows, const uint16_t* __restrict__ wgt, int32_t G,
+    int32_t K, int32_t Nout, const int32_t* __restrict__ tile_expert,
+    const int32_t* __restrict__ tile_row0, const int32_t* __restrict__ tile_rows,
+    uint16_t* __restrict__ y) {
   constexpr int NT = 2 * BN;                // threads
   constexpr int RS = NT / 8;                // rows staged per pass (8 threads per row)
   constexpr int AP = BM / RS;               // x rows per thread per step
@@ -134,10 +135,15 @@ __global__ __launch_bounds__(2 * BN) void grouped_gemm_kernel(
 
   int tile, jblk;
   gemm_block_order(blockIdx.x, Nout / BN, &tile, &jblk);
+  // Uniform exits: past the last tile (expert -1), or metadata that names no expert or
+  // no row of x.  Rows are clipped to [0, rows), so whatever the tile arrays hold,
+  // every access stays inside x, w and y.
   const int e = tile_expert[tile];
-  if (e < 0) return;  // uniform: past the last tile
+  if (e < 0 || e >= G) return;
   const int r0 = tile_row0[tile];
-  const int nrows = min(tile_rows[tile], BM);
+  if (r0 < 0 || r0 >= rows) return;
+  const int nrows = (int)min((int64_t)min(tile_rows[tile], BM), rows - r0);
+  if (nrows < 1) return;
   const int n0 = jblk * BN;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -309,17 +315,19 @@ hipError_t launch_gemm_tiles(const int32_t* expert_offset, const int32_t* expert
   return hipGetLastError();
 }
 
-hipError_t launch_grouped_gemm(const uint16_t* x, const uint16_t* w, int32_t K, int32_t Nout,
-                               const int32_t* tile_expert, const int32_t* tile_row0,
-                               const int32_t* tile_rows, int32_t max_tiles, uint16_t* y,
-                               hipStream_t stream) {
+hipError_t launch_grouped_gemm(const uint16_t* x, int64_t rows, const uint16_t* w, int32_t G,
+                               int32_t K, int32_t Nout, const int32_t* tile_expert,
+                               const int32_t* tile_row0, const int32_t* tile_rows,
+                               int32_t max_tiles, uint16_t* y, hipStream_t stream) {
   if (max_tiles == 0) return hipSuccess;
   if (Nout % 256 == 0) {
     hipLaunchKernelGGL((grouped_gemm_kernel<kBM, 256>), dim3((unsigned)(max_tiles * (Nout / 256))),
-                       dim3(512), 0, stream, x, w, K, Nout, tile_expert, tile_row0, tile_rows, y);
+                       dim3(512), 0, stream, x, rows, w, G, K, Nout, tile_expert, tile_row0,
+                       tile_rows, y);
   } else {
     hipLaunchKernelGGL((grouped_gemm_kernel<kBM, 128>), dim3((unsigned)(max_tiles * (Nout / 128))),
-                       dim3(256), 0, stream, x, w, K, Nout, tile_expert, tile_row0, tile_rows, y);
+                       dim3(256), 0, stream, x, rows, w, G, K, Nout, tile_expert, tile_row0,
+                       tile_rows, y);
   }
   return hipGetLastError();
 }

@@ -80,10 +80,10 @@ hipError_t launch_gemm_tiles(const int32_t* expert_offset, const int32_t* expert
                              int32_t tile_m, int32_t* tile_expert, int32_t* tile_row0,
                              int32_t* tile_rows, int32_t max_tiles, int32_t* num_tiles,
                              hipStream_t stream);
-hipError_t launch_grouped_gemm(const uint16_t* x, const uint16_t* w, int32_t K, int32_t Nout,
-                               const int32_t* tile_expert, const int32_t* tile_row0,
-                               const int32_t* tile_rows, int32_t max_tiles, uint16_t* y,
-                               hipStream_t stream);
+hipError_t launch_grouped_gemm(const uint16_t* x, int64_t rows, const uint16_t* w, int32_t G,
+                               int32_t K, int32_t Nout, const int32_t* tile_expert,
+                               const int32_t* tile_row0, const int32_t* tile_rows,
+                               int32_t max_tiles, uint16_t* y, hipStream_t stream);
 
 // ---------------------------------------------------------------- device helpers
 #if defined(__HIP_DEVICE_COMPILE__) || defined(__HIPCC__)

@@ -351,7 +351,10 @@ moe_status moe_grouped_gemm_tiles(const int32_t* expert_offset, const int32_t* e
  * Errors: MOE_ERR_INVALID_ARGUMENT (null or misaligned pointers, sizes < 1),
  * MOE_ERR_UNSUPPORTED (K % 64 != 0, Nout % 128 != 0, MOE_GEMM_TILE_M * K * 2 > 2^31 - 1,
  * max_tiles * Nout / 128 > 2^23),
- * MOE_ERR_LAUNCH.  The tile arrays are trusted: every tile's rows must lie in [0, rows).
+ * MOE_ERR_LAUNCH.  Tiles are checked on the device: a tile whose expert lies outside
+ * [0, G) or whose first row lies outside [0, rows) is skipped, and a tile's rows are
+ * clipped to end at row `rows`, so no tile arrays can make the kernel touch memory
+ * outside x, w and y.
  */
 moe_status moe_grouped_gemm(const uint16_t* x, int64_t rows, int32_t K, const uint16_t* w,
                             int32_t G, int32_t Nout, const int32_t* tile_expert,

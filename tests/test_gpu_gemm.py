@@ -132,3 +132,38 @@ def test_grouped_gemm_full_size_sampled(gpu_lib):
         mag[i] = magnitude(xs[i:i + 1], ws[i:i + 1], offs[:1], one[:1])[0]
     got = oracle.bf16_to_f32(host(y[dev(sample)]).view(np.uint16)).astype(np.float64)
     _bound_check(got, exact, mag, K, "full size")
+
+
+def test_grouped_gemm_bad_tiles(gpu_lib):
+    """Hand-made tile arrays holding an expert id past G, a negative one, a first row
+    past the end, a negative first row and a tile running past the last row: the bad
+    tiles are skipped, the long one is clipped at the last row, the valid ones are
+    computed, and rows no valid tile names keep their previous contents."""
+    rows, K, Nout, G = 200, 64, 128, 3
+    rng = np.random.default_rng(11)
+    x = _bf16(rng, (rows, K))
+    w = _bf16(rng, (G, Nout, K), scale=0.1)
+    tiles_h = [(0, 0, 128),      # valid
+               (3, 128, 62),     # expert == G: skipped
+               (1, 190, 128),    # runs past the last row: clipped to rows 190..199
+               (2, 250, 16),     # first row past the end: skipped
+               (-5, 128, 8),     # negative expert: skipped
+               (1, -3, 64)]      # negative first row: skipped
+    i32 = dict(dtype=torch.int32, device="cuda")
+    tiles = moedl.GemmTiles(torch.tensor([t[0] for t in tiles_h], **i32),
+                            torch.tensor([t[1] for t in tiles_h], **i32),
+                            torch.tensor([t[2] for t in tiles_h], **i32),
+                            torch.tensor([len(tiles_h)], **i32))
+    sentinel = 0x7FC1
+    y = torch.full((rows, Nout), sentinel, dtype=torch.int16, device="cuda")
+    moedl.moe_grouped_gemm(dev(x.view(np.int16)), dev(w.view(np.int16)), tiles, y=y)
+    torch.cuda.synchronize()
+    yh = host(y).view(np.uint16)
+    offs = np.array([0, 190, 0], dtype=np.int64)
+    cnts = np.array([128, 10, 0], dtype=np.int64)
+    exact = oracle.grouped_gemm(x, w, offs, cnts)
+    mag = magnitude(x, w, offs, cnts)
+    got = oracle.bf16_to_f32(yh).astype(np.float64)
+    for lo, hi in ((0, 128), (190, 200)):
+        _bound_check(got[lo:hi], exact[lo:hi], mag[lo:hi], K, f"rows {lo}..{hi}")
+    assert np.all(yh[128:190] == sentinel)
