@@ -100,6 +100,41 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return t.data_ptr() if t.numel() > 0 else None
 
 
+_I32 = (torch.int32,)
+_F32 = (torch.float32,)
+_ROW16 = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _want(t: Optional[torch.Tensor], name: str, dtypes, min_numel: int, cols: int = 0) -> None:
+    """Sizes reach the library separately from the tensors, so a tensor the kernels
+    index must hold at least min_numel elements of an accepted dtype (and, for row
+    buffers, `cols` columns), or the call is refused before any pointer is passed."""
+    if t is None:
+        return
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected one of {[str(d) for d in dtypes]}")
+    if cols and (t.dim() != 2 or t.shape[1] != cols):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected [rows, {cols}]")
+    if t.numel() < min_numel:
+        raise ValueError(f"{name}: {t.numel()} elements, the call needs {min_numel}")
+
+
+def _row_dtypes(x: torch.Tensor):
+    """Row buffers of one call share the element size of x."""
+    return _ROW16 if _dtype_code(x) == MOE_BF16 else (torch.uint8, torch.float8_e4m3fn)
+
+
+def _check_layout(lay: "Layout", M: int, k: int, G: int, B: int, dedup: bool) -> None:
+    _want(lay.expert_count, "expert_count", _I32, G)
+    _want(lay.expert_offset, "expert_offset", _I32, G)
+    _want(lay.bucket_count, "bucket_count", _I32, B)
+    _want(lay.bucket_offset, "bucket_offset", _I32, B + 1)
+    _want(lay.slot, "slot", _I32, M * k)
+    _want(lay.send_row, "send_row", _I32, M * k)
+    _want(lay.send_token, "send_token", _I32, send_capacity(M, k, B, dedup))
+    _want(lay.status, "status", _I32, 1)
+
+
 def _stream(stream) -> int:
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
@@ -159,6 +194,7 @@ def moe_dispatch_layout(topk_idx: torch.Tensor, expert_bucket: torch.Tensor, B: 
     if topk_idx.dtype != torch.int32 or expert_bucket.dtype != torch.int32:
         raise TypeError("topk_idx and expert_bucket must be int32")
     lay = out if out is not None else alloc_layout(M, k, G, B, dedup, topk_idx.device)
+    _check_layout(lay, M, k, G, B, dedup)
     st = lib().moe_dispatch_layout(
         _ptr(topk_idx), M, k, _ptr(expert_bucket), G, B, int(dedup), _ptr(lay.expert_count),
         _ptr(lay.expert_offset), _ptr(lay.bucket_count), _ptr(lay.bucket_offset),
@@ -189,6 +225,11 @@ def moe_dispatch(x: torch.Tensor, send_row: torch.Tensor, out_rows: int,
     if x_scale is not None and out_scale is None:
         out_scale = torch.empty((out_rows, x_scale.shape[1]), dtype=torch.float32,
                                 device=x.device)
+    sc = N // SCALE_BLOCK
+    _want(send_row, "send_row", _I32, M * k)
+    _want(out, "out", _row_dtypes(x), out_rows * N, cols=N)
+    _want(x_scale, "x_scale", _F32, M * sc)
+    _want(out_scale, "out_scale", _F32, out_rows * sc)
     st = lib().moe_dispatch(_ptr(x), _dtype_code(x), M, N, _ptr(x_scale), _ptr(send_row), k,
                             int(dedup), _ptr(out), _ptr(out_scale), out_rows, _stream(stream))
     _check("moe_dispatch", st)
@@ -211,11 +252,16 @@ def moe_layout_dispatch(topk_idx: torch.Tensor, expert_bucket: torch.Tensor, B: 
         raise TypeError("topk_idx and expert_bucket must be int32")
     if lay is None:
         lay = alloc_layout(M, k, G, B, dedup, topk_idx.device)
+    _check_layout(lay, M, k, G, B, dedup)
     rows = lay.capacity
     if out is None:
         out = torch.empty((rows, N), dtype=x.dtype, device=x.device)
     if x_scale is not None and out_scale is None:
         out_scale = torch.empty((rows, x_scale.shape[1]), dtype=torch.float32, device=x.device)
+    sc = N // SCALE_BLOCK
+    _want(out, "out", _row_dtypes(x), 0, cols=N)
+    _want(x_scale, "x_scale", _F32, M * sc)
+    _want(out_scale, "out_scale", _F32, out.shape[0] * sc)
     st = lib().moe_layout_dispatch(
         _ptr(topk_idx), M, k, _ptr(expert_bucket), G, B, int(dedup), _ptr(x), _dtype_code(x), N,
         _ptr(x_scale), _ptr(lay.expert_count), _ptr(lay.expert_offset), _ptr(lay.bucket_count),
@@ -230,10 +276,12 @@ def moe_combine(expert_out: torch.Tensor, weights: torch.Tensor, slot: torch.Ten
     """expert_out bf16 [rows, N], weights fp32 [M, k], slot int32 [M, k] -> y bf16 [M, N]."""
     rows, N = expert_out.shape
     M, k = slot.shape
-    if weights.dtype != torch.float32:
-        raise TypeError("weights must be float32")
+    _want(expert_out, "expert_out", _ROW16, 0)
+    _want(weights, "weights", _F32, M * k)
+    _want(slot, "slot", _I32, M * k)
     if y is None:
         y = torch.empty((M, N), dtype=expert_out.dtype, device=expert_out.device)
+    _want(y, "y", _ROW16, M * N, cols=N)
     st = lib().moe_combine(_ptr(expert_out), rows, _ptr(weights), _ptr(slot), M, k, N, _ptr(y),
                            _stream(stream))
     _check("moe_combine", st)
@@ -251,6 +299,12 @@ def moe_expand(recv: torch.Tensor, send_row: torch.Tensor, slot: torch.Tensor, e
     if recv_scale is not None and out_scale is None:
         out_scale = torch.empty((expert_rows, recv_scale.shape[1]), dtype=torch.float32,
                                 device=recv.device)
+    sc = N // SCALE_BLOCK
+    _want(send_row, "send_row", _I32, M * k)
+    _want(slot, "slot", _I32, M * k)
+    _want(out, "out", _row_dtypes(recv), expert_rows * N, cols=N)
+    _want(recv_scale, "recv_scale", _F32, R * sc)
+    _want(out_scale, "out_scale", _F32, expert_rows * sc)
     st = lib().moe_expand(_ptr(recv), _dtype_code(recv), R, N, _ptr(recv_scale), _ptr(send_row),
                           _ptr(slot), M, k, _ptr(out), _ptr(out_scale), expert_rows,
                           _stream(stream))
@@ -264,8 +318,13 @@ def moe_combine_partial(expert_out: torch.Tensor, weights: torch.Tensor, slot: t
     """Per-(token, bucket) partial sums, bf16 [partial_rows, N]."""
     rows, N = expert_out.shape
     M, k = slot.shape
+    _want(expert_out, "expert_out", _ROW16, 0)
+    _want(weights, "weights", _F32, M * k)
+    _want(slot, "slot", _I32, M * k)
+    _want(send_row, "send_row", _I32, M * k)
     if partial is None:
         partial = torch.empty((partial_rows, N), dtype=expert_out.dtype, device=expert_out.device)
+    _want(partial, "partial", _ROW16, partial_rows * N, cols=N)
     st = lib().moe_combine_partial(_ptr(expert_out), rows, _ptr(weights), _ptr(slot),
                                    _ptr(send_row), M, k, N, _ptr(partial), partial_rows,
                                    _stream(stream))
@@ -278,8 +337,11 @@ def moe_combine_reduce(partial: torch.Tensor, send_row: torch.Tensor,
     """y[t] = bf16(sum of the token's distinct partial rows, ascending)."""
     rows, N = partial.shape
     M, k = send_row.shape
+    _want(partial, "partial", _ROW16, 0)
+    _want(send_row, "send_row", _I32, M * k)
     if y is None:
         y = torch.empty((M, N), dtype=partial.dtype, device=partial.device)
+    _want(y, "y", _ROW16, M * N, cols=N)
     st = lib().moe_combine_reduce(_ptr(partial), rows, _ptr(send_row), M, k, N, _ptr(y),
                                   _stream(stream))
     _check("moe_combine_reduce", st)
@@ -290,8 +352,10 @@ def moe_expert_pair_counts(topk_idx: torch.Tensor, G: int, out: Optional[torch.T
                            stream=None) -> torch.Tensor:
     """Expert pair co-occurrence counts, int32 [G, G] on the device."""
     M, k = topk_idx.shape
+    _want(topk_idx, "topk_idx", _I32, M * k)
     if out is None:
         out = torch.empty((G, G), dtype=torch.int32, device=topk_idx.device)
+    _want(out, "pair_counts", _I32, G * G)
     st = lib().moe_expert_pair_counts(_ptr(topk_idx), M, k, G, _ptr(out), _stream(stream))
     _check("moe_expert_pair_counts", st)
     return out
@@ -303,6 +367,8 @@ def moe_place_experts(pair_counts, B: int):
     import numpy as np
     C = pair_counts.cpu().numpy() if isinstance(pair_counts, torch.Tensor) else pair_counts
     C = np.ascontiguousarray(C, dtype=np.int32)
+    if C.ndim != 2 or C.shape[0] != C.shape[1]:
+        raise ValueError(f"pair_counts: shape {C.shape}, expected [G, G]")
     G = C.shape[0]
     out = np.empty(G, dtype=np.int32)
     st = lib().moe_place_experts(C.ctypes.data, G, B, out.ctypes.data)
@@ -322,16 +388,26 @@ class GemmTiles:
         return self.expert.numel()
 
 
+def _check_tiles(t: GemmTiles) -> None:
+    _want(t.expert, "tile_expert", _I32, 0)
+    _want(t.row0, "tile_row0", _I32, t.max_tiles)
+    _want(t.rows, "tile_rows", _I32, t.max_tiles)
+    _want(t.num_tiles, "num_tiles", _I32, 1)
+
+
 def moe_grouped_gemm_tiles(expert_offset: torch.Tensor, expert_count: torch.Tensor, rows: int,
                            tile_m: int = GEMM_TILE_M, out: Optional[GemmTiles] = None,
                            stream=None) -> GemmTiles:
     """Row tiles of each expert's run, built on the device (no host sync)."""
     G = expert_count.numel()
+    _want(expert_count, "expert_count", _I32, G)
+    _want(expert_offset, "expert_offset", _I32, G)
     if out is None:
         mt = int(lib().moe_grouped_gemm_max_tiles(rows, G, tile_m))
         i32 = dict(dtype=torch.int32, device=expert_count.device)
         out = GemmTiles(torch.empty(mt, **i32), torch.empty(mt, **i32), torch.empty(mt, **i32),
                         torch.empty(1, **i32))
+    _check_tiles(out)
     st = lib().moe_grouped_gemm_tiles(_ptr(expert_offset), _ptr(expert_count), G, tile_m,
                                       _ptr(out.expert), _ptr(out.row0), _ptr(out.rows),
                                       out.max_tiles, _ptr(out.num_tiles), _stream(stream))
@@ -343,9 +419,15 @@ def moe_grouped_gemm(x: torch.Tensor, w: torch.Tensor, tiles: GemmTiles,
                      y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """y = per-expert x @ w[e].T (bf16 bits in and out, fp32 accumulation)."""
     rows, K = x.shape
-    G, Nout, _ = w.shape
+    G, Nout, Kw = w.shape
+    if Kw != K:
+        raise ValueError(f"w: shape {tuple(w.shape)}, expected [G, Nout, {K}]")
+    _want(x, "x", _ROW16, 0)
+    _want(w, "w", _ROW16, 0)
+    _check_tiles(tiles)
     if y is None:
         y = torch.empty((rows, Nout), dtype=x.dtype, device=x.device)
+    _want(y, "y", _ROW16, rows * Nout, cols=Nout)
     st = lib().moe_grouped_gemm(_ptr(x), rows, K, _ptr(w), G, Nout, _ptr(tiles.expert),
                                 _ptr(tiles.row0), _ptr(tiles.rows), tiles.max_tiles, _ptr(y),
                                 _stream(stream))

@@ -21,3 +21,11 @@ def gpu_lib():
     from combine_dispatch_layout_amd import moedl
     moedl.load()
     return moedl
+
+
+@pytest.fixture(scope="session")
+def built_lib():
+    """The HIP library loaded without touching a GPU: for host-side argument checks."""
+    from combine_dispatch_layout_amd import moedl
+    moedl.load()
+    return moedl
