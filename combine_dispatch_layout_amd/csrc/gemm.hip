@@ -14,9 +14,9 @@
 // arrays get expert -1 so a GEMM grid sized by the host-side bound simply exits there.
 //
 // grouped_gemm_kernel: one workgroup per (128-row tile, column block of 256, or of 128
-// when Nout is not a multiple of 256), details at the kernel.  Both operands are
-// K-contiguous ([rows, K] and [Nout, K]), which is what an MFMA lane needs: 8
-// consecutive k of one row or one column.  Accumulator lane layout of
+// when Nout is not a multiple of 256 or the grid would not fill the chip), details at
+// the kernel.  Both operands are K-contiguous ([rows, K] and [Nout, K]), which is what
+// an MFMA lane needs: 8 consecutive k of one row or one column.  Accumulator lane layout of
 // v_mfma_f32_32x32x16_bf16 (verified on the GPU): value v of lane l is
 // C[8*(v/4) + 4*(l/32) + v%4][l%32]; operand lane l holds A[l%32][8*(l/32) + i] and
 // B[8*(l/32) + i][l%32].
@@ -320,7 +320,14 @@ hipError_t launch_grouped_gemm(const uint16_t* x, int64_t rows, const uint16_t* 
                                const int32_t* tile_row0, const int32_t* tile_rows,
                                int32_t max_tiles, uint16_t* y, hipStream_t stream) {
   if (max_tiles == 0) return hipSuccess;
-  if (Nout % 256 == 0) {
+  // 256-column blocks move the fewest bytes per flop, but a grid of fewer workgroups
+  // than the chip's 256 CUs leaves CUs idle; then 128-column blocks (two workgroups per
+  // CU fit in LDS) double the grid.  Measured on MI355X, same outputs bit for bit: 16
+  // experts x 760 rows, K 2048 -> 768: 25.0 vs 19.8 us; 8 x 4096 rows, 4096 -> 1024:
+  // 60 vs 54 us; 64 x 8192 rows, 2048 -> 1024 (256 workgroups): 70 vs 81 us, so the
+  // switch is at the CU count.  The host only knows the bound max_tiles.
+  constexpr int64_t kCUs = 256;
+  if (Nout % 256 == 0 && (int64_t)max_tiles * (Nout / 256) >= kCUs) {
     hipLaunchKernelGGL((grouped_gemm_kernel<kBM, 256>), dim3((unsigned)(max_tiles * (Nout / 256))),
                        dim3(512), 0, stream, x, rows, w, G, K, Nout, tile_expert, tile_row0,
                        tile_rows, y);

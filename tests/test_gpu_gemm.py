@@ -167,3 +167,37 @@ def test_grouped_gemm_bad_tiles(gpu_lib):
     for lo, hi in ((0, 128), (190, 200)):
         _bound_check(got[lo:hi], exact[lo:hi], mag[lo:hi], K, f"rows {lo}..{hi}")
     assert np.all(yh[128:190] == sentinel)
+
+
+def test_grouped_gemm_column_blocks_agree(gpu_lib):
+    """A grid that would not fill the chip runs 128-column blocks, a large one
+    256-column blocks.  The same problem is driven through both, by sizing the tile
+    arrays to the exact bound (small grid) or padding them to 300 entries (unused
+    entries carry expert -1): the outputs must be identical bit for bit and within the
+    oracle's bound."""
+    G, rows, K, Nout = 16, 760, 256, 256
+    counts = np.full(G, rows // G, dtype=np.int64)
+    counts[: rows % G] += 1
+    idx = np.repeat(np.arange(G, dtype=np.int32), counts).reshape(-1, 1)
+    rng = np.random.default_rng(5)
+    idx = idx[rng.permutation(rows)]
+    ebkt = np.zeros(G, np.int32)
+    ref = oracle.dispatch_layout(idx, ebkt, 1, False)
+    lay = moedl.moe_dispatch_layout(dev(idx), dev(ebkt), 1, False)
+    small = _check_tiles(lay, ref, rows)
+    assert small.max_tiles * (Nout // 256) < 256
+    i32 = dict(dtype=torch.int32, device="cuda")
+    padded = moedl.GemmTiles(torch.empty(300, **i32), torch.empty(300, **i32),
+                             torch.empty(300, **i32), torch.empty(1, **i32))
+    moedl.moe_grouped_gemm_tiles(lay.expert_offset, lay.expert_count, rows, out=padded)
+    x = _bf16(rng, (rows, K))
+    w = _bf16(rng, (G, Nout, K), scale=0.1)
+    xd, wd = dev(x.view(np.int16)), dev(w.view(np.int16))
+    y_small = moedl.moe_grouped_gemm(xd, wd, small)
+    y_pad = moedl.moe_grouped_gemm(xd, wd, padded)
+    torch.cuda.synchronize()
+    assert torch.equal(y_small, y_pad)
+    exact = oracle.grouped_gemm(x, w, ref.expert_offset, ref.expert_count)
+    mag = magnitude(x, w, ref.expert_offset, ref.expert_count)
+    got = oracle.bf16_to_f32(host(y_small).view(np.uint16)).astype(np.float64)
+    _bound_check(got, exact, mag, K, "column blocks")
