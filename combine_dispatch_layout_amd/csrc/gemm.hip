@@ -13,10 +13,11 @@
 // in ascending id, tile_m rows each, the last shorter); unused entries of the tile
 // arrays get expert -1 so a GEMM grid sized by the host-side bound simply exits there.
 //
-// grouped_gemm_kernel: one workgroup per (128-row tile, column block of 256, or of 128
-// when Nout is not a multiple of 256 or the grid would not fill the chip), details at
-// the kernel.  Both operands are K-contiguous ([rows, K] and [Nout, K]), which is what
-// an MFMA lane needs: 8 consecutive k of one row or one column.  Accumulator lane layout of
+// grouped_gemm_kernel: one workgroup per (tile of up to 256 rows, column block of 256,
+// or of 128 when Nout is not a multiple of 256 or the grid would not fill the chip),
+// details at the kernel.  Both operands are K-contiguous ([rows, K] and [Nout, K]), which
+// is what an MFMA lane needs: 8 consecutive k of one row or one column.  Accumulator lane
+// layout of
 // v_mfma_f32_32x32x16_bf16 (verified on the GPU): value v of lane l is
 // C[8*(v/4) + 4*(l/32) + v%4][l%32]; operand lane l holds A[l%32][8*(l/32) + i] and
 // B[8*(l/32) + i][l%32].
@@ -27,7 +28,7 @@
 namespace moedl {
 namespace {
 
-constexpr int kBM = 128;   // rows per tile (one tile of moe_grouped_gemm_tiles)
+constexpr int kMaxBM = 256;  // rows per tile of moe_grouped_gemm_tiles (tile_m)
 constexpr int kBK = 64;    // k per pipeline step
 constexpr int kBufferWord3 = 0x00020000;  // raw buffer resource: no format, no swizzle
 constexpr int kPadK = kBK + 8;  // LDS row pitch in bf16: 16-byte fragment reads of
@@ -91,16 +92,17 @@ __device__ __forceinline__ void gemm_block_order(int bid, int nblk, int* tile, i
   *jblk = bid - *tile * nblk;
 }
 
-// One workgroup = one BM-row tile (BM = 128) x BN columns, 2 * BN / 64 waves: wave
-// (wm, wn) owns the BM/2 x 64 output block at rows wm*BM/2, columns wn*64, i.e. 2 x 2
+// One tile body = BM rows (128 or 256) x BN columns, 2 * BN / 64 waves: wave (wm, wn)
+// owns the BM/2 x 64 output block at rows wm*BM/2, columns wn*64, i.e. BM/64 x 2
 // accumulator blocks of 32 x 32.  With BN = 256 that is 8 waves, two per SIMD.
-// What bounds it (measured on the Zipf layout, random bf16): the kernel runs at ~0.87
-// PFLOP/s; with the global loads replaced by register constants (LDS writes kept) at
-// 1.38, with every load redirected to one tile so that all hit in L2 at 1.11, and with
-// the LDS writes dropped at 0.98.  So the global loads set the rate, about half through
-// the bytes each CU moves per flop and half through L2 misses to the fabric.  A 256-row
-// tile moves a third fewer bytes per flop: 1.05 vs 0.93 PFLOP/s on a uniform layout,
-// but on the Zipf layout its padding of short expert tiles eats the gain (0.88 useful).
+// What bounds it (measured on the Zipf layout with 128-row tiles, random bf16): the
+// kernel runs at ~0.87 PFLOP/s; with the global loads replaced by register constants
+// (LDS writes kept) at 1.38, with every load redirected to one tile so that all hit in
+// L2 at 1.11, and with the LDS writes dropped at 0.98.  So the global loads set the
+// rate, about half through the bytes each CU moves per flop and half through L2 misses
+// to the fabric.  Hence the 256-row body for full tiles: a third fewer bytes per flop.
+// With it (same process, outputs bit-identical): uniform layout 948 -> 1019 TFLOP/s,
+// Zipf 884 -> 904 (most Zipf experts have under 256 rows).
 // Short tiles (an expert's last rows): x is read through a buffer resource whose size
 // ends at the tile's last row, so rows past the end come back as zeros with no memory
 // traffic and every load stays unconditional.  (Skipping the MFMAs of 32-row blocks
@@ -110,7 +112,8 @@ __device__ __forceinline__ void gemm_block_order(int bid, int nblk, int* tile, i
 // double-buffered in registers across the four 16-wide k slices) while the tile of step
 // s+1, loaded into registers during step s-2, is written to buffer (s+1)%2 and the tile
 // of step s+3 is loaded into the registers it leaves: two register sets give the loads
-// two steps to arrive (2-3% faster than one step ahead, bit-identical output).  A wave
+// two steps to arrive (2-3% faster than one step ahead, bit-identical output; the
+// 256-row body keeps one set, loading step s+2, for lack of registers).  A wave
 // issues in order, so those LDS writes and global loads are placed between the MFMA
 // groups of the k slices (sched_barrier fences keep them there): the address unit then
 // works while the matrix cores do.  Issued after all of a step's MFMAs instead, they
@@ -118,33 +121,17 @@ __device__ __forceinline__ void gemm_block_order(int bid, int nblk, int* tile, i
 // branches (steps run in pairs so each register set is static; the last steps are
 // peeled), which keeps the compiler's memory wait counts exact.  One barrier per step
 // orders the two LDS buffers.
-template <int BM, int BN>
-__global__ __launch_bounds__(2 * BN) void grouped_gemm_kernel(
-    const uint16_t* __restrict__ x, int64_t rows, const uint16_t* __restrict__ wgt, int32_t G,
-    int32_t K, int32_t Nout, const int32_t* __restrict__ tile_expert,
-    const int32_t* __restrict__ tile_row0, const int32_t* __restrict__ tile_rows,
-    uint16_t* __restrict__ y) {
+template <int BM, int BN, int NSETS>
+__device__ __forceinline__ void gemm_tile(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wb, int32_t K, int32_t Nout,
+    int r0, int nrows, int n0, uint16_t (&As)[2][kMaxBM * kPadK],
+    uint16_t (&Bs)[2][BN * kPadK], uint16_t* __restrict__ y) {
   constexpr int NT = 2 * BN;                // threads
   constexpr int RS = NT / 8;                // rows staged per pass (8 threads per row)
   constexpr int AP = BM / RS;               // x rows per thread per step
   constexpr int BP = BN / RS;               // w rows per thread per step
   constexpr int WR = BM / 2;                // rows per wave
   constexpr int I = WR / 32, J = 2;         // 32 x 32 blocks per wave
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * kPadK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * kPadK];
-
-  int tile, jblk;
-  gemm_block_order(blockIdx.x, Nout / BN, &tile, &jblk);
-  // Uniform exits: past the last tile (expert -1), or metadata that names no expert or
-  // no row of x.  Rows are clipped to [0, rows), so whatever the tile arrays hold,
-  // every access stays inside x, w and y.
-  const int e = tile_expert[tile];
-  if (e < 0 || e >= G) return;
-  const int r0 = tile_row0[tile];
-  if (r0 < 0 || r0 >= rows) return;
-  const int nrows = (int)min((int64_t)min(tile_rows[tile], BM), rows - r0);
-  if (nrows < 1) return;
-  const int n0 = jblk * BN;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = wave_index();
@@ -153,14 +140,14 @@ __global__ __launch_bounds__(2 * BN) void grouped_gemm_kernel(
   // x through a buffer resource ending at the tile's last row: loads past it read 0
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(x + (int64_t)r0 * K), (short)0, nrows * K * 2, kBufferWord3);
-  const uint16_t* wb = wgt + ((int64_t)e * Nout + n0) * K;
 
   // global -> register staging: thread t moves the 16-byte chunk (t % 8) of rows
-  // t / 8 + RS p; eight consecutive threads cover one row's 128 bytes.  Two register
-  // sets: the tile of step s+1 is in set (s+1)%2 and that of step s+2 in set s%2.
+  // t / 8 + RS p; eight consecutive threads cover one row's 128 bytes.  With two
+  // register sets the tile of step s+1 is in set (s+1)%2 and that of step s+2 in set
+  // s%2; with one, the set holds the tile of step s+1 until it is written to LDS.
   const int lrow = tid >> 3;
   const int lcol = (tid & 7) * 8;
-  u32x4 ra[2][AP], rb[2][BP];
+  u32x4 ra[NSETS][AP], rb[NSETS][BP];
   auto load_a = [&](int set, int k0) {
 #pragma unroll
     for (int p = 0; p < AP; ++p) {
@@ -191,29 +178,40 @@ __global__ __launch_bounds__(2 * BN) void grouped_gemm_kernel(
     for (int j = 0; j < J; ++j) acc[i][j] = (f32x16_t){};
 
   const int steps = K / kBK;
-  load_a(0, 0);
-  load_b(0, 0, 0, BP);
-  if (steps > 1) {
-    load_a(1, kBK);
-    load_b(1, kBK, 0, BP);
-  }
-  store_a(0, 0);
-  store_b(0, 0);
-  if (steps > 2) {
-    load_a(0, 2 * kBK);
-    load_b(0, 2 * kBK, 0, BP);
+  if constexpr (NSETS == 2) {
+    load_a(0, 0);
+    load_b(0, 0, 0, BP);
+    if (steps > 1) {
+      load_a(1, kBK);
+      load_b(1, kBK, 0, BP);
+    }
+    store_a(0, 0);
+    store_b(0, 0);
+    if (steps > 2) {
+      load_a(0, 2 * kBK);
+      load_b(0, 2 * kBK, 0, BP);
+    }
+  } else {
+    load_a(0, 0);
+    load_b(0, 0, 0, BP);
+    store_a(0, 0);
+    store_b(0, 0);
+    if (steps > 1) {
+      load_a(0, kBK);
+      load_b(0, kBK, 0, BP);
+    }
   }
   __syncthreads();
-  // One k step on LDS buffer s%2.  NEXT: the tile of step s+1 (register set SET =
-  // (s+1)%2) is written to the other buffer; LOAD: the tile of step s+3 is then loaded
-  // into that set.  The loop below runs with both set and no branches in its body, so
-  // the compiler's wait counts stay exact; the last steps are peeled.
+  // One k step on LDS buffer s%2.  NEXT: the tile of step s+1 (in register set SET) is
+  // written to the other buffer; LOAD: the tile of step s + NSETS + 1 is then loaded
+  // into that set.  The loops below run with both set and no branches in their bodies,
+  // so the compiler's wait counts stay exact; the last steps are peeled.
   auto step = [&](int s, auto set_c, auto next_c, auto load_c) {
     constexpr int SET = decltype(set_c)::value;
     constexpr bool NEXT = decltype(next_c)::value;
     constexpr bool LOAD = decltype(load_c)::value;
     const int buf = s & 1;
-    const int k3 = (s + 3) * kBK;
+    const int kl = (s + NSETS + 1) * kBK;
     const uint16_t* Ab = As[buf] + (wm * WR + (lane & 31)) * kPadK + (lane >> 5) * 8;
     const uint16_t* Bb = Bs[buf] + (wn * 64 + (lane & 31)) * kPadK + (lane >> 5) * 8;
     bf16x8_t af[2][I], bfr[2][J];
@@ -232,25 +230,25 @@ __global__ __launch_bounds__(2 * BN) void grouped_gemm_kernel(
                                                               0, 0, 0);
     };
     load_frags(0, 0);
-    // k slice 0: write the x part of step s+1, then load the x part of step s+3
+    // k slice 0: write the x part of step s+1, then load the x part of a later step
     load_frags(1, 1);
     mfmas(0);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (NEXT) store_a(SET, buf ^ 1);
-    if constexpr (LOAD) load_a(SET, k3);
+    if constexpr (LOAD) load_a(SET, kl);
     __builtin_amdgcn_sched_barrier(0);
-    // k slice 1: write the w part of step s+1, load half of the w part of step s+3
+    // k slice 1: write the w part of step s+1, load half of the later step's w part
     load_frags(2, 0);
     mfmas(1);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (NEXT) store_b(SET, buf ^ 1);
-    if constexpr (LOAD) load_b(SET, k3, 0, BP / 2);
+    if constexpr (LOAD) load_b(SET, kl, 0, BP / 2);
     __builtin_amdgcn_sched_barrier(0);
     // k slice 2: the other half of the w loads
     load_frags(3, 1);
     mfmas(0);
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (LOAD) load_b(SET, k3, BP / 2, BP);
+    if constexpr (LOAD) load_b(SET, kl, BP / 2, BP);
     __builtin_amdgcn_sched_barrier(0);
     // k slice 3
     mfmas(1);
@@ -260,31 +258,38 @@ __global__ __launch_bounds__(2 * BN) void grouped_gemm_kernel(
   using no = std::false_type;
   using set0 = std::integral_constant<int, 0>;
   using set1 = std::integral_constant<int, 1>;
-  // pairs of steps (s even, then s + 1), so the register set of each is static
-  int s = 0;
-  for (; s + 4 < steps; s += 2) {
-    step(s, set1{}, yes{}, yes{});
-    step(s + 1, set0{}, yes{}, yes{});
-  }
-  switch (steps - s) {  // 1 to 4 steps left, s even
-    case 4:
+  if constexpr (NSETS == 2) {
+    // pairs of steps (s even, then s + 1), so the register set of each is static
+    int s = 0;
+    for (; s + 4 < steps; s += 2) {
       step(s, set1{}, yes{}, yes{});
-      step(s + 1, set0{}, yes{}, no{});
-      step(s + 2, set1{}, yes{}, no{});
-      step(s + 3, set0{}, no{}, no{});
-      break;
-    case 3:
-      step(s, set1{}, yes{}, no{});
-      step(s + 1, set0{}, yes{}, no{});
-      step(s + 2, set1{}, no{}, no{});
-      break;
-    case 2:
-      step(s, set1{}, yes{}, no{});
-      step(s + 1, set0{}, no{}, no{});
-      break;
-    default:
-      step(s, set1{}, no{}, no{});
-      break;
+      step(s + 1, set0{}, yes{}, yes{});
+    }
+    switch (steps - s) {  // 1 to 4 steps left, s even
+      case 4:
+        step(s, set1{}, yes{}, yes{});
+        step(s + 1, set0{}, yes{}, no{});
+        step(s + 2, set1{}, yes{}, no{});
+        step(s + 3, set0{}, no{}, no{});
+        break;
+      case 3:
+        step(s, set1{}, yes{}, no{});
+        step(s + 1, set0{}, yes{}, no{});
+        step(s + 2, set1{}, no{}, no{});
+        break;
+      case 2:
+        step(s, set1{}, yes{}, no{});
+        step(s + 1, set0{}, no{}, no{});
+        break;
+      default:
+        step(s, set1{}, no{}, no{});
+        break;
+    }
+  } else {
+    int s = 0;
+    for (; s + 2 < steps; ++s) step(s, set0{}, yes{}, yes{});
+    if (s + 1 < steps) step(s++, set0{}, yes{}, no{});
+    step(s, set0{}, no{}, no{});
   }
 
   // epilogue: fp32 -> bf16 (round to nearest even), rows past the tile end skipped
@@ -301,9 +306,56 @@ __global__ __launch_bounds__(2 * BN) void grouped_gemm_kernel(
       }
 }
 
-}  // namespace
+// Workgroup -> (tile, column block) -> one of two tile bodies.  Tiles hold up to 256 rows
+// (moe_grouped_gemm_tiles with tile_m = 256): a tile of more than 128 rows runs the
+// 256-row body, which moves a third fewer bytes per flop, with one register set (two
+// would not fit beside its accumulators); a tile of at most 128 rows runs the 128-row
+// body with two register sets.  An expert's rows are thus padded to a multiple of 128,
+// as with 128-row tiles, while its full 256-row blocks take the cheaper body.  The
+// branch is uniform over the workgroup and taken once.  SPLIT (grids too small to fill
+// the chip): two workgroups per tile, each running the 128-row body on one half.
+template <int BN, bool SPLIT>
+__global__ __launch_bounds__(2 * BN) void grouped_gemm_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, const uint16_t* __restrict__ wgt, int32_t G,
+    int32_t K, int32_t Nout, const int32_t* __restrict__ tile_expert,
+    const int32_t* __restrict__ tile_row0, const int32_t* __restrict__ tile_rows,
+    uint16_t* __restrict__ y) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][kMaxBM * kPadK];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * kPadK];
+  int tile, jblk, half = 0;
+  if constexpr (SPLIT) {
+    int unit;
+    gemm_block_order(blockIdx.x, Nout / BN, &unit, &jblk);
+    tile = unit >> 1;
+    half = unit & 1;
+  } else {
+    gemm_block_order(blockIdx.x, Nout / BN, &tile, &jblk);
+  }
+  // Uniform exits: past the last tile (expert -1), or metadata that names no expert or
+  // no row of x.  Rows are clipped to [0, rows), so whatever the tile arrays hold,
+  // every access stays inside x, w and y.
+  const int e = tile_expert[tile];
+  if (e < 0 || e >= G) return;
+  int r0 = tile_row0[tile];
+  if (r0 < 0 || r0 >= rows) return;
+  int nrows = (int)min((int64_t)min(tile_rows[tile], kMaxBM), rows - r0);
+  const int n0 = jblk * BN;
+  const uint16_t* wb = wgt + ((int64_t)e * Nout + n0) * K;
+  if constexpr (SPLIT) {
+    r0 += half * (kMaxBM / 2);
+    nrows = min(nrows - half * (kMaxBM / 2), kMaxBM / 2);
+    if (nrows < 1) return;
+    gemm_tile<kMaxBM / 2, BN, 2>(x, wb, K, Nout, r0, nrows, n0, As, Bs, y);
+  } else {
+    if (nrows < 1) return;
+    if (nrows > kMaxBM / 2)
+      gemm_tile<kMaxBM, BN, 1>(x, wb, K, Nout, r0, nrows, n0, As, Bs, y);
+    else
+      gemm_tile<kMaxBM / 2, BN, 2>(x, wb, K, Nout, r0, nrows, n0, As, Bs, y);
+  }
+}
 
-int32_t gemm_tile_rows() { return kBM; }
+}  // namespace
 
 hipError_t launch_gemm_tiles(const int32_t* expert_offset, const int32_t* expert_count, int32_t G,
                              int32_t tile_m, int32_t* tile_expert, int32_t* tile_row0,
@@ -320,21 +372,29 @@ hipError_t launch_grouped_gemm(const uint16_t* x, int64_t rows, const uint16_t* 
                                const int32_t* tile_row0, const int32_t* tile_rows,
                                int32_t max_tiles, uint16_t* y, hipStream_t stream) {
   if (max_tiles == 0) return hipSuccess;
-  // 256-column blocks move the fewest bytes per flop, but a grid of fewer workgroups
-  // than the chip's 256 CUs leaves CUs idle; then 128-column blocks (two workgroups per
-  // CU fit in LDS) double the grid.  Measured on MI355X, same outputs bit for bit: 16
-  // experts x 760 rows, K 2048 -> 768: 25.0 vs 19.8 us; 8 x 4096 rows, 4096 -> 1024:
-  // 60 vs 54 us; 64 x 8192 rows, 2048 -> 1024 (256 workgroups): 70 vs 81 us, so the
-  // switch is at the CU count.  The host only knows the bound max_tiles.
+  // Three launch shapes, by how far the grid fills the chip's 256 CUs (the host knows
+  // only the bound max_tiles):
+  //  - 256-column blocks move the fewest bytes per flop: used when that grid has at
+  //    least one workgroup per CU;
+  //  - else 128-column blocks, which double the grid;
+  //  - else 128-column blocks with each tile split over two workgroups (128 rows each),
+  //    four times the 256-column grid.
+  // Measured on MI355X, same outputs bit for bit: 16 experts x 760 rows, K 2048 -> 768:
+  // 25.0 us with 256-column blocks vs 19.8 with 128-column ones; 8 x 4096 rows, 4096 ->
+  // 1024: 60 vs 54 us; but 64 x 8192 rows, 2048 -> 1024 (256 workgroups): 70 vs 81 us,
+  // hence the switch at the CU count.
   constexpr int64_t kCUs = 256;
-  if (Nout % 256 == 0 && (int64_t)max_tiles * (Nout / 256) >= kCUs) {
-    hipLaunchKernelGGL((grouped_gemm_kernel<kBM, 256>), dim3((unsigned)(max_tiles * (Nout / 256))),
-                       dim3(512), 0, stream, x, rows, w, G, K, Nout, tile_expert, tile_row0,
-                       tile_rows, y);
+  const int64_t grid256 = Nout % 256 == 0 ? (int64_t)max_tiles * (Nout / 256) : 0;
+  const int64_t grid128 = (int64_t)max_tiles * (Nout / 128);
+  if (grid256 >= kCUs) {
+    hipLaunchKernelGGL((grouped_gemm_kernel<256, false>), dim3((unsigned)grid256), dim3(512), 0,
+                       stream, x, rows, w, G, K, Nout, tile_expert, tile_row0, tile_rows, y);
+  } else if (grid128 >= kCUs) {
+    hipLaunchKernelGGL((grouped_gemm_kernel<128, false>), dim3((unsigned)grid128), dim3(256), 0,
+                       stream, x, rows, w, G, K, Nout, tile_expert, tile_row0, tile_rows, y);
   } else {
-    hipLaunchKernelGGL((grouped_gemm_kernel<kBM, 128>), dim3((unsigned)(max_tiles * (Nout / 128))),
-                       dim3(256), 0, stream, x, rows, w, G, K, Nout, tile_expert, tile_row0,
-                       tile_rows, y);
+    hipLaunchKernelGGL((grouped_gemm_kernel<128, true>), dim3((unsigned)(2 * grid128)), dim3(256),
+                       0, stream, x, rows, w, G, K, Nout, tile_expert, tile_row0, tile_rows, y);
   }
   return hipGetLastError();
 }

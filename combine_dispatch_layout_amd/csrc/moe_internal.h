@@ -75,7 +75,6 @@ hipError_t launch_pair_counts(const int32_t* topk_idx, int64_t M, int32_t k, int
 
 void place_experts_greedy(const int32_t* pair_counts, int32_t G, int32_t B, int32_t* bucket);
 
-int32_t gemm_tile_rows();
 hipError_t launch_gemm_tiles(const int32_t* expert_offset, const int32_t* expert_count, int32_t G,
                              int32_t tile_m, int32_t* tile_expert, int32_t* tile_row0,
                              int32_t* tile_rows, int32_t max_tiles, int32_t* num_tiles,

@@ -61,7 +61,7 @@ SIGNATURES = {
         _vp, _i64, _i32, _vp, _i32, _i32, _i32p, _i32p, _i32p, _i32, _vp, _vp]),
 }
 
-GEMM_TILE_M = 128
+GEMM_TILE_M = 256
 
 
 class MoeError(RuntimeError):

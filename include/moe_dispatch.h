@@ -320,7 +320,7 @@ moe_status moe_place_experts(const int32_t* pair_counts, int32_t G, int32_t B,
  * map computed on the device, weights in their native [E, N, K] layout).
  * ---------------------------------------------------------------------------------
  */
-#define MOE_GEMM_TILE_M 128 /* rows per tile moe_grouped_gemm expects */
+#define MOE_GEMM_TILE_M 256 /* rows per tile moe_grouped_gemm expects (tile_m) */
 
 /* Host-side bound on the number of row tiles: ceil(rows / tile_m) + G. */
 int32_t moe_grouped_gemm_max_tiles(int64_t rows, int32_t G, int32_t tile_m);
@@ -346,8 +346,12 @@ moe_status moe_grouped_gemm_tiles(const int32_t* expert_offset, const int32_t* e
  * of a tile of expert e, fp32 accumulation on the matrix cores
  * (v_mfma_f32_32x32x16_bf16).
  *   x  bf16 [rows, K] (slot-indexed expert inputs), w bf16 [G, Nout, K],
- *   tiles from moe_grouped_gemm_tiles with tile_m = MOE_GEMM_TILE_M,
+ *   tiles from moe_grouped_gemm_tiles with tile_m = MOE_GEMM_TILE_M (any tiling with at
+ *   most MOE_GEMM_TILE_M rows per tile gives the same y; rows of a tile past that many
+ *   are not computed),
  *   y  bf16 [rows, Nout]; rows outside every tile are not written.
+ *   Every element is the same whichever of the kernel's launch shapes runs: each output
+ *   element is one lane's k-ordered fp32 accumulation.
  * Errors: MOE_ERR_INVALID_ARGUMENT (null or misaligned pointers, sizes < 1),
  * MOE_ERR_UNSUPPORTED (K % 64 != 0, Nout % 128 != 0, MOE_GEMM_TILE_M * K * 2 > 2^31 - 1,
  * max_tiles * Nout / 128 > 2^23),

@@ -190,7 +190,7 @@ def test_grouped_gemm_tiles_argument_errors(kw, status):
     (dict(mt=-1), INVALID), (dict(w=None), INVALID), (dict(te=None), INVALID),
     (dict(x=None), INVALID), (dict(y=None), INVALID), (dict(x=P + 2), INVALID),
     (dict(w=P + 8), INVALID), (dict(K=7160), UNSUPPORTED), (dict(Nout=2000), UNSUPPORTED),
-    (dict(K=1 << 23), UNSUPPORTED),
+    (dict(K=1 << 23), UNSUPPORTED), (dict(K=1 << 22), UNSUPPORTED),  # 256-row tile offsets
     (dict(mt=1 << 21, Nout=1024), UNSUPPORTED), (dict(rows=0, x=None, y=None), OK),
 ])
 def test_grouped_gemm_argument_errors(kw, status):

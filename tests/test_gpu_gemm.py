@@ -134,70 +134,82 @@ def test_grouped_gemm_full_size_sampled(gpu_lib):
     _bound_check(got, exact, mag, K, "full size")
 
 
-def test_grouped_gemm_bad_tiles(gpu_lib):
+def _tiles_of(entries, size=None):
+    """GemmTiles holding the given (expert, first row, rows) entries, padded with expert
+    -1 to `size` entries."""
+    size = size or len(entries)
+    pad = [(-1, 0, 0)] * (size - len(entries))
+    i32 = dict(dtype=torch.int32, device="cuda")
+    cols = list(zip(*(list(entries) + pad)))
+    return moedl.GemmTiles(torch.tensor(cols[0], **i32), torch.tensor(cols[1], **i32),
+                           torch.tensor(cols[2], **i32), torch.tensor([len(entries)], **i32))
+
+
+@pytest.mark.parametrize("size", [6, 260])
+def test_grouped_gemm_bad_tiles(gpu_lib, size):
     """Hand-made tile arrays holding an expert id past G, a negative one, a first row
     past the end, a negative first row and a tile running past the last row: the bad
     tiles are skipped, the long one is clipped at the last row, the valid ones are
-    computed, and rows no valid tile names keep their previous contents."""
-    rows, K, Nout, G = 200, 64, 128, 3
+    computed, and rows no valid tile names keep their previous contents.  Six entries
+    launch the split shape (128-row halves), 260 the whole-tile shape (256-row body)."""
+    rows, K, Nout, G = 400, 64, 128, 3
     rng = np.random.default_rng(11)
     x = _bf16(rng, (rows, K))
     w = _bf16(rng, (G, Nout, K), scale=0.1)
-    tiles_h = [(0, 0, 128),      # valid
-               (3, 128, 62),     # expert == G: skipped
-               (1, 190, 128),    # runs past the last row: clipped to rows 190..199
-               (2, 250, 16),     # first row past the end: skipped
-               (-5, 128, 8),     # negative expert: skipped
-               (1, -3, 64)]      # negative first row: skipped
-    i32 = dict(dtype=torch.int32, device="cuda")
-    tiles = moedl.GemmTiles(torch.tensor([t[0] for t in tiles_h], **i32),
-                            torch.tensor([t[1] for t in tiles_h], **i32),
-                            torch.tensor([t[2] for t in tiles_h], **i32),
-                            torch.tensor([len(tiles_h)], **i32))
+    tiles = _tiles_of([(0, 0, 128),      # valid
+                       (3, 128, 62),     # expert == G: skipped
+                       (1, 190, 256),    # runs past the last row: clipped to rows 190..399
+                       (2, 450, 16),     # first row past the end: skipped
+                       (-5, 128, 8),     # negative expert: skipped
+                       (1, -3, 64)],     # negative first row: skipped
+                      size)
     sentinel = 0x7FC1
     y = torch.full((rows, Nout), sentinel, dtype=torch.int16, device="cuda")
     moedl.moe_grouped_gemm(dev(x.view(np.int16)), dev(w.view(np.int16)), tiles, y=y)
     torch.cuda.synchronize()
     yh = host(y).view(np.uint16)
     offs = np.array([0, 190, 0], dtype=np.int64)
-    cnts = np.array([128, 10, 0], dtype=np.int64)
+    cnts = np.array([128, 210, 0], dtype=np.int64)
     exact = oracle.grouped_gemm(x, w, offs, cnts)
     mag = magnitude(x, w, offs, cnts)
     got = oracle.bf16_to_f32(yh).astype(np.float64)
-    for lo, hi in ((0, 128), (190, 200)):
+    for lo, hi in ((0, 128), (190, 400)):
         _bound_check(got[lo:hi], exact[lo:hi], mag[lo:hi], K, f"rows {lo}..{hi}")
     assert np.all(yh[128:190] == sentinel)
 
 
-def test_grouped_gemm_column_blocks_agree(gpu_lib):
-    """A grid that would not fill the chip runs 128-column blocks, a large one
-    256-column blocks.  The same problem is driven through both, by sizing the tile
-    arrays to the exact bound (small grid) or padding them to 300 entries (unused
-    entries carry expert -1): the outputs must be identical bit for bit and within the
-    oracle's bound."""
-    G, rows, K, Nout = 16, 760, 256, 256
-    counts = np.full(G, rows // G, dtype=np.int64)
-    counts[: rows % G] += 1
-    idx = np.repeat(np.arange(G, dtype=np.int32), counts).reshape(-1, 1)
+def test_grouped_gemm_launch_shapes_agree(gpu_lib):
+    """The kernel has three launch shapes, chosen by how far the grid fills the chip:
+    256-column blocks, 128-column blocks, and 128-column blocks with every tile split
+    over two workgroups.  One problem, with experts whose row counts straddle the 128-
+    and 256-row bodies, is driven through all three by sizing the tile arrays (the exact
+    bound, 200 entries, 300 entries; unused entries carry expert -1): the outputs must
+    be identical bit for bit and within the oracle's bound."""
+    counts = [0, 1, 127, 128, 129, 300, 0, 5, 255, 256, 257, 33, 96, 97, 520]
+    G, K, Nout = len(counts), 192, 256
+    idx = np.concatenate([np.full(c, e, np.int32) for e, c in enumerate(counts)]).reshape(-1, 1)
     rng = np.random.default_rng(5)
-    idx = idx[rng.permutation(rows)]
+    idx = idx[rng.permutation(len(idx))]
+    rows = len(idx)
     ebkt = np.zeros(G, np.int32)
     ref = oracle.dispatch_layout(idx, ebkt, 1, False)
     lay = moedl.moe_dispatch_layout(dev(idx), dev(ebkt), 1, False)
-    small = _check_tiles(lay, ref, rows)
-    assert small.max_tiles * (Nout // 256) < 256
+    exact_size = _check_tiles(lay, ref, rows)
+    assert exact_size.max_tiles * (Nout // 128) < 256                  # split shape
+    outs = [exact_size]
     i32 = dict(dtype=torch.int32, device="cuda")
-    padded = moedl.GemmTiles(torch.empty(300, **i32), torch.empty(300, **i32),
-                             torch.empty(300, **i32), torch.empty(1, **i32))
-    moedl.moe_grouped_gemm_tiles(lay.expert_offset, lay.expert_count, rows, out=padded)
+    for size in (200, 300):                       # 128-column, then 256-column blocks
+        t = moedl.GemmTiles(torch.empty(size, **i32), torch.empty(size, **i32),
+                            torch.empty(size, **i32), torch.empty(1, **i32))
+        outs.append(moedl.moe_grouped_gemm_tiles(lay.expert_offset, lay.expert_count, rows,
+                                                 out=t))
     x = _bf16(rng, (rows, K))
     w = _bf16(rng, (G, Nout, K), scale=0.1)
     xd, wd = dev(x.view(np.int16)), dev(w.view(np.int16))
-    y_small = moedl.moe_grouped_gemm(xd, wd, small)
-    y_pad = moedl.moe_grouped_gemm(xd, wd, padded)
+    ys = [moedl.moe_grouped_gemm(xd, wd, t) for t in outs]
     torch.cuda.synchronize()
-    assert torch.equal(y_small, y_pad)
+    assert torch.equal(ys[0], ys[1]) and torch.equal(ys[0], ys[2])
     exact = oracle.grouped_gemm(x, w, ref.expert_offset, ref.expert_count)
     mag = magnitude(x, w, ref.expert_offset, ref.expert_count)
-    got = oracle.bf16_to_f32(host(y_small).view(np.uint16)).astype(np.float64)
-    _bound_check(got, exact, mag, K, "column blocks")
+    got = oracle.bf16_to_f32(host(ys[0]).view(np.uint16)).astype(np.float64)
+    _bound_check(got, exact, mag, K, "launch shapes")
