@@ -16,10 +16,11 @@ import pytest
 import torch
 
 import oracle
+from combine_dispatch_layout_amd import moedl
 from combine_dispatch_layout_amd import workloads as wl
-from gpu_util import (assert_bits_equal, assert_dispatch_equal, assert_layout_equal, dev,
-                      gpu_combine, gpu_dispatch, gpu_expert_outputs, gpu_layout, host,
-                      oracle_combine_tokens, oracle_pipeline, say)
+from gpu_util import (SENTINEL_BF16, SENTINEL_FP8, assert_bits_equal, assert_dispatch_equal,
+                      assert_layout_equal, dev, gpu_combine, gpu_dispatch, gpu_expert_outputs,
+                      gpu_layout, host, oracle_combine_tokens, oracle_pipeline, rows_dev, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -237,3 +238,33 @@ def test_deterministic_and_stream_ordered(gpu_lib):
         y = gpu_combine(w, lay, out)
     s.synchronize()
     assert np.array_equal(host(y), results[0][2])
+
+
+@pytest.mark.parametrize("cfg,M,dedup", [(3, 2048, False), (3, 2048, True), (5, 1024, False),
+                                         (4, 1536, True)])
+def test_dispatch_shapes_agree(gpu_lib, cfg, M, dedup):
+    """Launch geometry must not change any output: moe_dispatch's two kernel shapes (k
+    single-store waves, or two waves sharing a token's distinct rows; its dedup flag
+    picks the shape) write identical bytes, scales included, for a layout of either
+    mode."""
+    w = wl.make_workload(cfg, M=M)
+    say(f"dispatch shapes {w.name} M={M} dedup-layout={dedup}")
+    lay = gpu_layout(w, dedup)
+    x = rows_dev(w)
+    xs = dev(w.x_scale) if w.x_scale is not None else None
+    outs = []
+    for shape_flag in (False, True):
+        out = torch.full((lay.capacity, w.N), SENTINEL_BF16 if w.dtype == "bf16" else SENTINEL_FP8,
+                         dtype=x.dtype, device="cuda")
+        osc = (torch.full((lay.capacity, xs.shape[1]), float("nan"), device="cuda")
+               if xs is not None else None)
+        moedl.moe_dispatch(x, lay.send_row, lay.capacity, xs, out=out, out_scale=osc,
+                           dedup=shape_flag)
+        outs.append((out, osc))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0])
+    if xs is not None:
+        assert torch.equal(outs[0][1].isnan(), outs[1][1].isnan())
+        assert torch.equal(torch.nan_to_num(outs[0][1]), torch.nan_to_num(outs[1][1]))
+    ref = oracle.dispatch_layout(w.topk_idx, w.expert_bucket, w.B, dedup)
+    assert_dispatch_equal(w, outs[0][0], outs[0][1], ref, ctx=w.name)
