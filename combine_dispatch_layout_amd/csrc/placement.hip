@@ -107,8 +107,11 @@ void place_experts_greedy(const int32_t* C, int32_t G, int32_t B, int32_t* bucke
   const int cap = G / B;
   std::vector<int> parent(G), size(G, 1);
   for (int e = 0; e < G; ++e) parent[e] = e;
-  auto find = [&](int a) {
-    while (parent[a] != a) a = parent[a];
+  auto find = [&](int a) {  // with path halving; the roots, hence the result, are unchanged
+    while (parent[a] != a) {
+      parent[a] = parent[parent[a]];
+      a = parent[a];
+    }
     return a;
   };
 
