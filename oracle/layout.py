@@ -15,7 +15,7 @@ Test infrastructure only.  What is computed, and where it comes from:
 * "Purlin ...", section 3.1 (Layouts): the send buffer is scattered-V, partitions
   indexed by destination with variable sizes.
 
-Readings where the pages are silent (each one is also listed in the design notes):
+Readings where the pages are silent:
 
 * Experts are laid out in memory ordered by (bucket, expert id); with a contiguous
   map that is plain ascending id.
