@@ -70,8 +70,12 @@ __global__ __launch_bounds__(256) void standin_kernel(
 }
 
 // One 16-byte vector per thread over a full grid: the fastest plain copy shape
-// measured on MI355X (~6.5 TB/s read+write at 2 GiB; a persistent grid-stride loop
-// reaches ~4.8 TB/s).
+// measured on MI355X (a persistent grid-stride loop reaches ~4.8 TB/s).  The launch
+// requests kCopyLds bytes of (unused) dynamic LDS per workgroup, which caps residency
+// at five workgroups per CU: fastest at 2 GiB, 6.74 TB/s read+write against 6.56 with
+// no cap (sweep of the reservation: 24-30 KiB best, 32 KiB and more slower).
+constexpr unsigned kCopyLds = 30 * 1024;
+
 __global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src,
                                                    u32x4* __restrict__ dst, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -102,7 +106,7 @@ extern "C" int moe_harness_copy(const void* src, void* dst, size_t bytes, hipStr
   const int64_t n = (int64_t)(bytes / 16);
   const int64_t blocks = (n + 255) / 256;
   if (blocks > 0x7FFFFFFF) return 1;
-  hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (const u32x4*)src,
-                     (u32x4*)dst, n);
+  hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks), dim3(256), kCopyLds, stream,
+                     (const u32x4*)src, (u32x4*)dst, n);
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }
