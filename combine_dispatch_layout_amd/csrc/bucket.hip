@@ -56,8 +56,9 @@ __device__ __forceinline__ u32x4 to_bf16x8(const float (&acc)[8]) {
 // ------------------------------------------------------------------ expand
 // NW = k/2 waves, wave w copies entries j = w, w + NW (two 16-byte loads in flight,
 // then two stores).  Measured on MI355X (Zipf M=16384 dedup): ~5.7 TB/s, against
-// ~4.5 for k single-entry waves.
-template <int K, int NW>
+// ~4.5 for k single-entry waves.  Scales travel only in the SCALES instantiation (a
+// run-time test costs the rows-only dispatch 3%; the same split is kept here).
+template <int K, int NW, bool SCALES>
 __global__ __launch_bounds__(64 * NW) void expand_kernel(
     const u32x4* __restrict__ recv, int64_t recv_rows, int32_t row_vecs, int32_t pieces,
     const float* __restrict__ recv_scale, int32_t scale_cols,
@@ -89,7 +90,7 @@ __global__ __launch_bounds__(64 * NW) void expand_kernel(
     if (!ok[h]) continue;
     if (c < row_vecs)
       __builtin_nontemporal_store(v[h], ein + (int64_t)dst[h] * row_vecs + c);
-    if (recv_scale != nullptr && piece == 0) {
+    if (SCALES && piece == 0) {
       const int r = send_row[t * K + w + h * NW];
       for (int sc = lane; sc < scale_cols; sc += 64)
         ein_scale[(int64_t)dst[h] * scale_cols + sc] = recv_scale[(int64_t)r * scale_cols + sc];
@@ -269,9 +270,16 @@ hipError_t launch_expand_k(const void* recv, int64_t recv_rows, int32_t row_vecs
                            const int32_t* slot, int64_t M, void* expert_in, float* expert_scale,
                            int64_t expert_rows, hipStream_t stream) {
   constexpr int NW = K >= 2 ? K / 2 : 1;
-  hipLaunchKernelGGL((expand_kernel<K, NW>), dim3((unsigned)(M * pieces)), dim3(64 * NW), 0,
-                     stream, (const u32x4*)recv, recv_rows, row_vecs, pieces, recv_scale,
-                     scale_cols, send_row, slot, M, (u32x4*)expert_in, expert_scale, expert_rows);
+  if (recv_scale != nullptr)
+    hipLaunchKernelGGL((expand_kernel<K, NW, true>), dim3((unsigned)(M * pieces)), dim3(64 * NW),
+                       0, stream, (const u32x4*)recv, recv_rows, row_vecs, pieces, recv_scale,
+                       scale_cols, send_row, slot, M, (u32x4*)expert_in, expert_scale,
+                       expert_rows);
+  else
+    hipLaunchKernelGGL((expand_kernel<K, NW, false>), dim3((unsigned)(M * pieces)), dim3(64 * NW),
+                       0, stream, (const u32x4*)recv, recv_rows, row_vecs, pieces, recv_scale,
+                       scale_cols, send_row, slot, M, (u32x4*)expert_in, expert_scale,
+                       expert_rows);
   return hipGetLastError();
 }
 
