@@ -112,8 +112,21 @@ __global__ __launch_bounds__(64 * NW) void combine_partial_kernel(
   if (t >= M) return;  // uniform over the workgroup
   const int c = piece * kPieceVecs + lane;
   const int cc = c < row_vecs ? c : row_vecs - 1;
-  const int32_t* srow = slot + t * K;
-  const int32_t* rrow = send_row + t * K;
+  // The token's slot, send-row and weight rows, read first (wave-uniform scalar loads,
+  // all in flight together while the data loads travel; read after the barrier they
+  // would cost a dependent round trip each).  The empty asm keeps the compiler from
+  // sinking the loads of values only used after the barrier.
+  int srow[K], rrow[K];
+  float wrow[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    srow[j] = slot[t * K + j];
+    rrow[j] = send_row[t * K + j];
+    wrow[j] = wts[t * K + j];
+  }
+#pragma unroll
+  for (int j = 0; j < K; ++j) asm volatile("" : "+s"(rrow[j]), "+s"(wrow[j]));
+  asm volatile("" : "+s"(partial), "+s"(partial_rows));
 
   // stage the k source pieces.  Loads are unconditional, so all of a lane's loads are
   // in flight together: an invalid slot reads row 0 (in bounds whenever any row
@@ -161,7 +174,7 @@ __global__ __launch_bounds__(64 * NW) void combine_partial_kernel(
     for (int jj = 0; jj < K; ++jj) {
       if (jj < j || rrow[jj] != r) continue;
       const int s = srow[jj];
-      accumulate(acc, stage[jj][lane], (s >= 0 && s < expert_rows) ? wts[t * K + jj] : 0.0f);
+      accumulate(acc, stage[jj][lane], (s >= 0 && s < expert_rows) ? wrow[jj] : 0.0f);
     }
     __builtin_nontemporal_store(to_bf16x8(acc), partial + (int64_t)r * row_vecs + c);
   }
