@@ -28,7 +28,7 @@
 // kernel runs the Zipf workload above in 313 instead of 323 us (6.74 TB/s, the
 // plain-copy ceiling) and correlated pairs (4 KiB rows) in 94 instead of 97 us.
 //
-// With a dedup layout (the caller says so), or a send buffer above 3 GiB, a second
+// With a dedup layout (the caller says so), or a send buffer above 2 GiB, a second
 // shape is used, below.  Both shapes write the same bytes.
 #include "moe_internal.h"
 
@@ -137,12 +137,13 @@ hipError_t launch_dispatch(const void* x, int64_t M, int64_t row_bytes, const fl
   const int32_t pieces = (row_vecs + kPieceVecs - 1) / kPieceVecs;
   const int64_t blocks = M * pieces;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  // The k single-store waves shape is the faster one for send buffers up to ~2 GB
-  // (Zipf, 16384 tokens x 14 KiB x 8: 6.4 vs 6.0 TB/s), but with a send buffer of
-  // ~3.8 GB or more (65536 tokens x 8 x 7 KiB, or x 14 KiB) it falls to ~3.6 TB/s while
-  // the shape of two waves sharing a token's rows holds ~5.3 TB/s (measured on MI355X,
-  // with and without scales, fp8 and bf16 alike).  So large buffers take that shape too.
-  constexpr int64_t kSharedShapeBytes = (int64_t)3 << 30;
+  // The k single-store waves shape is the faster one for send buffers up to 2 GiB
+  // (6.3-6.7 vs 5.8-6.1 TB/s from 0.5 to 2.11 GB, uniform and Zipf routing), but past
+  // 2 GiB it falls to ~3.7-3.8 TB/s (2.35, 2.82 and 3.76 GB send buffers, bf16 and fp8,
+  // with and without scales) while the shape of two waves sharing a token's rows holds
+  // ~5.2-5.5 TB/s (measured on MI355X; the store addresses are full 64-bit, so the cliff
+  // is the memory system's, not an offset's).  So large buffers take that shape too.
+  constexpr int64_t kSharedShapeBytes = (int64_t)2 << 30;
   if (dedup || out_rows * row_bytes > kSharedShapeBytes) {
 #define MOEDL_CASE(K)                                                                          \
   case K:                                                                                      \

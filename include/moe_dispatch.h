@@ -140,7 +140,7 @@ moe_status moe_dispatch_layout(const int32_t* topk_idx, int64_t M, int32_t k,
  *   dedup     0 or 1: whether send_row came from a dedup layout.  Only selects the
  *             kernel shape (k single-store waves per row piece, or two waves sharing
  *             the token's distinct rows; the latter also for send buffers above
- *             3 GiB); the bytes written are the same.
+ *             2 GiB); the bytes written are the same.
  * Outputs:
  *   out       [out_rows, N] elements of `dtype`; rows named by send_row are written.
  *   out_scale float [out_rows, N/128]; NULL exactly when x_scale is NULL.
