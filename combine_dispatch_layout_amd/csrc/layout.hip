@@ -509,7 +509,12 @@ __global__ __launch_bounds__(kTileThreads) void layout_single_kernel(
 // inside the buffer.  `idx` must be readable at index 0 even when M = 0.
 constexpr int kFusedPieceVecs = kTileThreads;  // 16-byte vectors per work item
 constexpr int kFusedBatch = 4;                  // work items loaded together
-constexpr int kFusedMaxBlocks = 256;            // one workgroup per CU
+// Grid cap: two workgroups per CU, which fit at once for every instantiation (41-68 KiB
+// of LDS each).  Every workgroup recomputes the layout before copying, so a grid that
+// does not fit at once pays that again in a second wave.  Measured (graph replay,
+// layout + dispatch + combine, N=7168, top-8): cap 256 / 512 / 1024 -> 27.4 / 23.1 /
+// 30.5 us at M=256, 47.6 / 38.4 / 51.7 us at M=512, equal at M <= 128.
+constexpr int kFusedMaxBlocks = 512;
 
 template <int KC, int NTILE, int NC>
 __global__ __launch_bounds__(kTileThreads) void layout_dispatch_small_kernel(
