@@ -50,8 +50,10 @@ KERNEL_SOURCES = {
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
+    # 100 timed and 20 warm-up iterations: the event-loop method of "All2all performance
+    # comparison between Triton-distributed and DeepEP" ("Test Code Snippet")
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--dedup", action="store_true", help="time dedup mode instead")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay leg")
@@ -62,7 +64,10 @@ def parse():
                          "gemm: grouped-GEMM tile metadata + the MFMA grouped GEMM; "
                          "small: latency at M <= 512, fused layout+dispatch vs three calls")
     ap.add_argument("--nout", type=int, default=2048, help="grouped GEMM output width")
-    ap.add_argument("--cfg", type=int, default=3, help=argparse.SUPPRESS)
+    ap.add_argument("--cfg", type=int, default=3, choices=[1, 2, 3, 4, 5],
+                    help="workload: 1 uniform M=64; 2 uniform M=4096, scaled experts; "
+                         "3 Zipf M=16384 (the headline); 4 correlated pairs, N=2048, G=128; "
+                         "5 uniform M=65536 fp8 with scales")
     return ap.parse_args()
 
 
