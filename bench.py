@@ -15,7 +15,7 @@ Collectives" (section 5: 128 invocations captured in a graph, one warm-up replay
 eight timed replays, divided by 1,024), a plain copy-kernel ceiling, and the CPU
 oracle timed on the same inputs.
 
-    python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--dedup] [--no-cpu]
+    python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--cfg 1-5] [--dedup] [--no-cpu]
     python bench.py --path bucket    # dedup round trip: layout, dispatch, moe_expand,
                                      # moe_combine_partial, moe_combine_reduce
     python bench.py --path placement --cfg 4   # pair counts, greedy placement, savings
