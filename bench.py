@@ -97,6 +97,27 @@ def recorded_traffic(kernel: str, workload: str, path: Optional[str] = None):
         return None
 
 
+def host_cores() -> str:
+    cpu_model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return f"1 of {len(os.sched_getaffinity(0))} host cores ({cpu_model})"
+
+
+def hbm_roofline(kernel: str, alg_bytes: float, launch_us: float, traffic=None, **extra):
+    achieved = alg_bytes / (launch_us * 1e-6) / 1e9
+    r = {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+         "alg_bytes_per_launch": int(alg_bytes), "launch_us": round(launch_us, 2)}
+    r.update(extra)
+    return r
+
+
 def cpu_baseline(w, dedup: bool, max_tokens: int = 16384):
     """The oracle as it stands, single-threaded, on the same inputs: layout, dispatch
     and combine on the first min(M, max_tokens) tokens (the whole workload up to 16384
@@ -121,19 +142,11 @@ def cpu_baseline(w, dedup: bool, max_tokens: int = 16384):
     dt = (t1 - t0) + (t2 - t1) + (t4 - t3)
     scale_bytes = xs.shape[1] * 4 if xs is not None else 0
     alg = (Ms + lay.R) * (w.row_bytes + scale_bytes) + (Ms * w.k + Ms) * w.N * 2
-    cpu_model = "unknown"
-    try:
-        for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                cpu_model = line.split(":", 1)[1].strip()
-                break
-    except OSError:
-        pass
     return {
         "value": round(alg / dt / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
         "sample": (f"{'whole workload' if Ms == w.M else 'first'} {Ms} tokens, one pass of "
                    f"layout+dispatch+combine ({dt:.2f} s; stand-in expert step excluded), "
-                   f"1 of {len(os.sched_getaffinity(0))} host cores ({cpu_model})"),
+                   f"{host_cores()}"),
         "seconds": round(dt, 3),
         "phase_seconds": {"layout": round(t1 - t0, 3), "dispatch": round(t2 - t1, 3),
                           "combine": round(t4 - t3, 3)},
@@ -191,6 +204,10 @@ def bench_bucket(args, w, dev):
     # identity experts, weights summing to one: y is x to within two bf16 roundings
     diff = (y.view(torch.bfloat16).float() - x.view(torch.bfloat16).float()).abs()
     assert bool((diff <= x.view(torch.bfloat16).float().abs() * (2 * 2.0 ** -8) + 1e-30).all().item())
+    # roofline of the slowest data-moving kernel of the round trip
+    dom = max((n for n in names if rows[n]), key=lambda n: per[n])
+    roofline = hbm_roofline(dom, rows[dom] * rb, per[dom] * 1e3)
+    cpu = None if args.no_cpu else cpu_bucket_baseline(w, 8192)
     res = {"metric": METRIC + " [dedup round trip]", "value": round(total / (ms * 1e-3) / 1e9, 1),
            "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
            "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
@@ -200,8 +217,38 @@ def bench_bucket(args, w, dev):
            "us_per_step": round(ms * 1e3, 2), "alg_bytes_per_step": total,
            "event_us": {n: round(per[n] * 1e3, 2) for n in names},
            "kernel_gbps": {n: round(rows[n] * rb / (per[n] * 1e-3) / 1e9, 1)
-                           for n in names if rows[n]}}
+                           for n in names if rows[n]},
+           "roofline": roofline, "cpu_baseline": cpu}
     print(json.dumps(res))
+
+
+def cpu_bucket_baseline(w, max_tokens: int):
+    """The oracle's dedup round trip (layout, dispatch, expand, combine_partial,
+    combine_reduce), single-threaded, on the first min(M, max_tokens) tokens."""
+    import oracle
+    Ms = min(w.M, max_tokens)
+    idx, x, wts = w.topk_idx[:Ms], w.x[:Ms], w.weights[:Ms]
+    k, rb = w.k, w.row_bytes
+    t = [time.perf_counter()]
+    lay = oracle.dispatch_layout(idx, w.expert_bucket, w.B, True)
+    t.append(time.perf_counter())
+    sent, _ = oracle.dispatch(x, lay.send_row, lay.R)
+    t.append(time.perf_counter())
+    ein, _ = oracle.expand(sent, lay.send_row, lay.slot, Ms * k)
+    t.append(time.perf_counter())
+    part = oracle.combine_partial(ein, wts, lay.slot, lay.send_row, lay.R)
+    t.append(time.perf_counter())
+    oracle.combine_reduce(part, lay.send_row)
+    t.append(time.perf_counter())
+    dt = t[-1] - t[0]
+    R = lay.R
+    alg = ((Ms + R) + (R + Ms * k) + (Ms * k + R) + (R + Ms)) * rb
+    names = ["layout", "dispatch", "expand", "combine_partial", "combine_reduce"]
+    return {"value": round(alg / dt / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": (f"{'whole workload' if Ms == w.M else 'first'} {Ms} tokens, one pass of "
+                       f"the dedup round trip ({dt:.2f} s), {host_cores()}"),
+            "seconds": round(dt, 3),
+            "phase_seconds": {n: round(t[i + 1] - t[i], 3) for i, n in enumerate(names)}}
 
 
 def bench_placement(args, w, dev):
@@ -246,12 +293,27 @@ def bench_placement(args, w, dev):
         lay = moedl.moe_dispatch_layout(idx[h:].contiguous(), torch.from_numpy(m).to(dev), B, True)
         torch.cuda.synchronize()
         holdout[name] = round(1 - int(lay.bucket_offset[B].item()) / ((M - h) * k), 4)
+    # pair counts: read the routing table once, write the G x G counts
+    roofline = hbm_roofline("pair_counts", M * k * 4 + G * G * 4, counts_us)
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        t0 = time.perf_counter()
+        Co = oracle.pair_counts(w.topk_idx, G)
+        t1 = time.perf_counter()
+        omap = oracle.greedy_place(Co, B)
+        t2 = time.perf_counter()
+        cpu = {"value": round((t1 - t0) * 1e6, 1), "unit": "us (pair counts)", "cores": 1,
+               "kind": "oracle", "greedy_ms": round((t2 - t1) * 1e3, 3),
+               "same_map_as_library": bool(np.array_equal(omap, greedy)),
+               "sample": f"whole workload, M={M}, G={G}, one pass, {host_cores()}"}
     res = {"metric": "expert placement: dedup saving (fraction of token copies removed)",
            "value": saving["greedy"], "unit": "fraction", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "higher_is_better": True, "vs_baseline": None,
            "data": "synthetic", "config": {"workload": w.name, "M": M, "G": G, "k": k, "B": B},
            "send_rows": rows, "dedup_saving": saving, "dedup_saving_second_half": holdout,
-           "pair_counts_us": round(counts_us, 2), "greedy_host_ms": round(greedy_ms, 3)}
+           "pair_counts_us": round(counts_us, 2), "greedy_host_ms": round(greedy_ms, 3),
+           "roofline": roofline, "cpu_baseline": cpu}
     print(json.dumps(res))
 
 
@@ -337,6 +399,8 @@ def bench_gemm(args, w, dev):
     torch.cuda.synchronize()
     del src, dst
 
+    cpu = None if args.no_cpu else cpu_gemm_baseline(w, wt, Nout, 8192)
+
     wl_name = f"{w.name}-grouped-gemm-K{N}-N{Nout}"
     traffic = recorded_traffic("grouped_gemm", wl_name,
                                os.path.join(PROFILES, f"hbm_traffic_{wl_name}.txt"))
@@ -351,11 +415,40 @@ def bench_gemm(args, w, dev):
                         "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
                         "min_hbm_bytes_per_launch": int(G * Nout * N * 2 + M * k * N * 2
                                                         + M * k * Nout * 2)},
+           "cpu_baseline": cpu,
            "event_us": {"grouped_gemm_tiles": round(t_tiles, 2), "grouped_gemm": round(t_gemm, 2)},
            "deepspeed_page_shape": {"experts": Gs, "tokens": Ms, "K": Ks, "Nout": Ns,
                                     "tiles_us": round(s_tiles, 2), "gemm_us": round(s_gemm, 2),
                                     "tflops": round(2.0 * Ms * Ks * Ns / (s_gemm * 1e-6) / 1e12, 2)}}
     print(json.dumps(res))
+
+
+def cpu_gemm_baseline(w, wt, Nout: int, sample_rows: int):
+    """The oracle's grouped GEMM (float64 products), one BLAS thread, on the first
+    `sample_rows` rows of the per-expert layout.  Its inputs come from the oracle's own
+    layout and dispatch of the host tokens; the weights of the experts those rows
+    belong to are copied from the device tensor the GPU leg uses."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    lay = oracle.dispatch_layout(w.topk_idx, w.expert_bucket, w.B, False)
+    S = min(sample_rows, w.M * w.k)
+    xe, _ = oracle.dispatch(w.x, lay.send_row, w.M * w.k)
+    off = lay.expert_offset.astype(np.int64)
+    cnt = np.clip(np.minimum(off + lay.expert_count, S) - off, 0, None)
+    experts = np.nonzero(cnt)[0]
+    x_s = np.ascontiguousarray(xe[:S])
+    del xe
+    w_s = wt[experts.tolist()].cpu().numpy().view(np.uint16)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        oracle.grouped_gemm(x_s, w_s, off[experts], cnt[experts])
+        dt = time.perf_counter() - t0
+    return {"value": round(2.0 * S * w.N * Nout / dt / 1e12, 5), "unit": "TFLOP/s", "cores": 1,
+            "kind": "oracle",
+            "sample": (f"first {S} of {w.M * w.k} rows of the per-expert layout "
+                       f"({len(experts)} experts), K={w.N}, Nout={Nout}, float64 products "
+                       f"({dt:.2f} s), {host_cores()}"),
+            "seconds": round(dt, 3)}
 
 
 def graph_replay_us(torch, step, invocations=128, timed=8):
@@ -429,15 +522,54 @@ def bench_small(args, dev):
                 res[f"{tag}_{name}_graph_us"] = round(graph_replay_us(torch, fn), 2)
                 xz = torch.where(x == -32768, torch.zeros_like(x), x)
                 assert bool((y == xz).all().item()), f"M={M} {tag} {name}: y != x"
+            if M == 64 and not dedup:
+                # per-kernel event times of the fused step, for the roofline
+                stream = torch.cuda.current_stream()
+                ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+                      for _ in range(args.steps)]
+                for e in ev:
+                    e[0].record(stream)
+                    moedl.moe_layout_dispatch(idx, ebkt, B, False, x, lay=lay, out=out)
+                    e[1].record(stream)
+                    moedl.moe_combine(eo, wts, lay.slot, y=y)
+                    e[2].record(stream)
+                torch.cuda.synchronize()
+                ld_us = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e3
+                cb_us = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e3
+                kern = {"layout_dispatch": (ld_us, (M + M * k) * w.row_bytes),
+                        "combine": (cb_us, (M * k + M) * N * 2)}
+                dom = max(kern, key=lambda n: kern[n][0])
+                roofline = hbm_roofline(dom, kern[dom][1], kern[dom][0],
+                                        event_us={n: round(v[0], 2) for n, v in kern.items()})
         rows.append(res)
     head = rows[0]
+    cpu = None if args.no_cpu else cpu_small_baseline(workloads.make_workload(1, M=64))
     out = {"metric": "small-M layout+dispatch+combine latency (graph replay, us per step)",
            "value": head["flat_fused_graph_us"], "unit": "us", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "higher_is_better": False, "scaling": "weak",
            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
            "config": {"workload": "uniform-top8-N7168-G256-B8", "M": [r["M"] for r in rows]},
-           "rows": rows}
+           "roofline": roofline, "cpu_baseline": cpu, "rows": rows}
     print(json.dumps(out))
+
+
+def cpu_small_baseline(w, seconds: float = 3.0):
+    """The oracle's layout + dispatch + combine at the small workload's M, repeated for
+    about `seconds`; microseconds per step, single-threaded."""
+    import oracle
+    n, t0 = 0, time.perf_counter()
+    while True:
+        lay = oracle.dispatch_layout(w.topk_idx, w.expert_bucket, w.B, False)
+        sent, _ = oracle.dispatch(w.x, lay.send_row, lay.R)
+        oracle.combine(sent, w.weights, lay.slot)
+        n += 1
+        dt = time.perf_counter() - t0
+        if dt >= seconds:
+            break
+    return {"value": round(dt * 1e6 / n, 1), "unit": "us", "cores": 1, "kind": "oracle",
+            "sample": (f"M={w.M} flat layout+dispatch+combine, {n} repetitions ({dt:.2f} s), "
+                       f"{host_cores()}"),
+            "seconds": round(dt, 3)}
 
 
 def main():
