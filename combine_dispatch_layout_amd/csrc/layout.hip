@@ -504,9 +504,13 @@ __global__ __launch_bounds__(kTileThreads) void layout_single_kernel(
 // none ever waits for another; workgroup 0 alone writes the layout arrays.  Then the
 // workgroups share the row copies: work item i = (token, 4 KiB piece of its row) goes to
 // workgroup i mod gridDim.x, which loads the piece once (a batch of items at a time, all
-// loads in flight; the first batch is issued before the layout work, which hides its
-// latency) and stores it non-temporally to each of the token's distinct send rows
-// inside the buffer.  `idx` must be readable at index 0 even when M = 0.
+// loads in flight) and stores it non-temporally to each of the token's distinct send
+// rows inside the buffer.  The LDS row table holds each distinct row once (dedup repeats
+// are marked absent while the layout is built), so the scatter reads a token's k rows
+// together and needs no duplicate search.  Issuing the first batch of row loads before
+// the layout work was measured slower (vector-load counters retire in order, so the
+// layout's first wait on topk_idx also waited on the rows).  `idx` must be readable at
+// index 0 even when M = 0.
 constexpr int kFusedPieceVecs = kTileThreads;  // 16-byte vectors per work item
 constexpr int kFusedBatch = 4;                  // work items loaded together
 // Grid cap: two workgroups per CU, which fit at once for every instantiation (41-68 KiB
@@ -545,8 +549,6 @@ __global__ __launch_bounds__(kTileThreads) void layout_dispatch_small_kernel(
   const int64_t Mk = (int64_t)M * k;
   const bool writer = blockIdx.x == 0;
 
-  // The rows do not depend on the layout: the first batch of row loads is issued
-  // now and lands while the layout is computed.
   const int64_t items = (int64_t)M * pieces;
   const int64_t stride = gridDim.x;
   u32x4 v[kFusedBatch];
@@ -560,7 +562,6 @@ __global__ __launch_bounds__(kTileThreads) void layout_dispatch_small_kernel(
       v[q] = x[in_row ? t * row_vecs + c : 0];
     }
   };
-  if (items > 0) load_batch(blockIdx.x);  // uniform; x may be null only when M = 0
 
   if (tid < kMaxB) bsum_s[tid] = 0;
   if (tid == 0) {
@@ -640,7 +641,11 @@ __global__ __launch_bounds__(kTileThreads) void layout_dispatch_small_kernel(
             const int b = eb[tile][j];
             const int r = b != kBadBucket ? boff_s[b] + dl[tile][j] + (tile > 0 ? tb_s[0][b] : 0)
                                           : -1;
-            row_s[t * k + j] = r;
+            // a later entry of a bucket already seen has the same row: absent here
+            bool repeat = false;
+#pragma unroll
+            for (int jj = 0; jj < KC; ++jj) repeat |= jj < j && eb[tile][jj] == b;
+            row_s[t * k + j] = repeat ? -1 : r;
             if (writer) {
               send_row[(int64_t)t * k + j] = r;
               if (r >= 0 && r < cap) send_token[r] = t;
@@ -654,7 +659,7 @@ __global__ __launch_bounds__(kTileThreads) void layout_dispatch_small_kernel(
 
   // row scatter
   for (int64_t base = blockIdx.x; base < items; base += stride * kFusedBatch) {
-    if (base != (int64_t)blockIdx.x) load_batch(base);
+    load_batch(base);  // x may be null only when M = 0, and then there is no item
 #pragma unroll
     for (int q = 0; q < kFusedBatch; ++q) {
       const int64_t it = base + q * stride;
@@ -663,11 +668,13 @@ __global__ __launch_bounds__(kTileThreads) void layout_dispatch_small_kernel(
       const int piece = (int)(it - (int64_t)t * pieces);
       const int c = piece * kFusedPieceVecs + tid;
       const int32_t* rows = row_s + t * k;
-      for (int j = 0; j < k; ++j) {
-        const int r = rows[j];
-        bool first = r >= 0 && r < out_rows;
-        for (int jj = 0; jj < j; ++jj) first = first && rows[jj] != r;
-        if (!first) continue;  // uniform
+      int rr[KC];
+#pragma unroll
+      for (int j = 0; j < KC; ++j) rr[j] = j < k ? rows[j] : -1;
+#pragma unroll
+      for (int j = 0; j < KC; ++j) {
+        const int r = rr[j];
+        if (r < 0 || r >= out_rows) continue;  // uniform
         if (c < row_vecs) __builtin_nontemporal_store(v[q], out + (int64_t)r * row_vecs + c);
         if (x_scale != nullptr && piece == 0) {
           for (int sc = tid; sc < scale_cols; sc += kTileThreads)
