@@ -13,9 +13,11 @@
 // in ascending id, tile_m rows each, the last shorter); unused entries of the tile
 // arrays get expert -1 so a GEMM grid sized by the host-side bound simply exits there.
 //
-// grouped_gemm_kernel: one workgroup per (tile of up to 256 rows, column block of 256,
-// or of 128 when Nout is not a multiple of 256 or the grid would not fill the chip),
-// details at the kernel.  Both operands are K-contiguous ([rows, K] and [Nout, K]), which
+// grouped_gemm_kernel / grouped_gemm_direct_kernel: one workgroup per (tile of up to 256
+// rows, column block of 256, or of 128 when Nout is not a multiple of 256 or the grid
+// would not fill the chip), details at the kernels.  The direct kernel (operands copied
+// global -> LDS with no register staging) runs when K % 128 == 0 and the grid fills the
+// chip; the register-staged one otherwise.  Both operands are K-contiguous ([rows, K] and [Nout, K]), which
 // is what an MFMA lane needs: 8 consecutive k of one row or one column.  Accumulator lane
 // layout of
 // v_mfma_f32_32x32x16_bf16 (verified on the GPU): value v of lane l is
@@ -355,6 +357,195 @@ __global__ __launch_bounds__(2 * BN) void grouped_gemm_kernel(
   }
 }
 
+// ------------------------------------------------- direct-to-LDS body (K % 128 == 0)
+// The same tile (BM rows x BN columns, 2 * BN / 64 waves, wave (wm, wn) owning BM/2 x 64)
+// and the same MFMA sequence per output element as gemm_tile, so the outputs are
+// identical bit for bit; only the way the operands reach LDS differs.  Each 64-wide k
+// step of x and w is copied global -> LDS by buffer_load ... lds (16 bytes per lane, no
+// registers, no LDS write instructions): one wave instruction fills 1 KiB of LDS, lane L
+// at byte 16 L, which is 8 rows of 128 bytes.  The rows are not padded; instead lane L
+// fetches the global chunk (L % 8) ^ ((row >> 1) & 7) of its row, an XOR swizzle under
+// which the 16 lanes of each fragment read group hit 16 distinct 16-byte bank slots.
+// Two LDS stages, each its own array so the compiler can tell a fragment read of one
+// stage from the loads in flight into the other: step s waits for its own loads (issued
+// during step s - 1), passes the barrier, issues step s + 1 into the other stage and runs
+// its MFMAs.  Measured (Zipf layout, 131072 rows, K 7168 -> 2048; the register-staged
+// body, same run): loads kept but fragment reads dropped 1.07 PFLOP/s, fragment reads
+// kept but loads dropped 1.68, MFMAs alone 2.02, so the global loads still set the rate;
+// four stages of k = 32 (loads three steps ahead) ran slower than two stages of 64.
+typedef __attribute__((address_space(3))) void lds_void_t;
+constexpr int kChunkBf16 = 8;  // bf16 per 16-byte chunk
+
+template <int BM, int BN>
+__device__ __forceinline__ void gemm_tile_direct(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wb, int32_t K, int32_t Nout,
+    int r0, int nrows, int n0, uint16_t (&A0)[kMaxBM * kBK], uint16_t (&A1)[kMaxBM * kBK],
+    uint16_t (&B0)[BN * kBK], uint16_t (&B1)[BN * kBK], uint16_t* __restrict__ y) {
+  constexpr int NWV = 2 * BN / 64;         // waves
+  constexpr int QA = BM / 8, QB = BN / 8;  // 8-row (1 KiB) load instructions per stage
+  static_assert(QA % NWV == 0 && QB % NWV == 0, "whole load instructions per wave");
+  constexpr int PA = QA / NWV, PB = QB / NWV;
+  constexpr int WR = BM / 2;
+  constexpr int I = WR / 32, J = 2;
+  const int lane = threadIdx.x & 63;
+  const int w = wave_index();
+  const int wm = w & 1, wn = w >> 1;
+
+  // x through a buffer resource ending at the tile's last row (loads past it read 0),
+  // w through one covering the BN x K block
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(x + (int64_t)r0 * K), (short)0, nrows * K * 2, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)wb, (short)0, BN * K * 2, kBufferWord3);
+  // wave w issues instructions q = w, w + NWV, ...; lane L of instruction q loads row
+  // 8 q + L / 8, global chunk (L % 8) ^ swizzle: byte offsets at k = 0
+  const int lr = lane >> 3, pos = lane & 7;
+  int va[PA], vb[PB];
+#pragma unroll
+  for (int p = 0; p < PA; ++p) {
+    const int row = (p * NWV + w) * 8 + lr;
+    va[p] = (row * K + (pos ^ ((row >> 1) & 7)) * kChunkBf16) * 2;
+  }
+#pragma unroll
+  for (int p = 0; p < PB; ++p) {
+    const int row = (p * NWV + w) * 8 + lr;
+    vb[p] = (row * K + (pos ^ ((row >> 1) & 7)) * kChunkBf16) * 2;
+  }
+  auto issue = [&](auto stage_c, int k0) {
+#if defined(__HIP_DEVICE_COMPILE__)  // LDS address-space pointers exist in the device pass only
+    constexpr int ST = decltype(stage_c)::value;
+    uint16_t* Ad = ST == 0 ? A0 : A1;
+    uint16_t* Bd = ST == 0 ? B0 : B1;
+#pragma unroll
+    for (int p = 0; p < PA; ++p)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void_t*)(Ad + (p * NWV + w) * 8 * kBK), 16,
+                                               va[p] + k0 * 2, 0, 0, 0);
+#pragma unroll
+    for (int p = 0; p < PB; ++p)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_void_t*)(Bd + (p * NWV + w) * 8 * kBK), 16,
+                                               vb[p] + k0 * 2, 0, 0, 0);
+#endif
+  };
+
+  f32x16_t acc[I][J];
+#pragma unroll
+  for (int i = 0; i < I; ++i)
+#pragma unroll
+    for (int j = 0; j < J; ++j) acc[i][j] = (f32x16_t){};
+
+  // fragment reads: row R = (multiple of 32) + lane % 32, so the swizzle of every row a
+  // lane reads is (lane >> 1) & 7; k slice kk holds chunks 2 kk (lanes 0-31), 2 kk + 1
+  const int sw = (lane >> 1) & 7, hi = lane >> 5;
+  auto step = [&](int s, auto stage_c, auto next_c) {
+    constexpr int ST = decltype(stage_c)::value;
+    constexpr bool NEXT = decltype(next_c)::value;
+    const uint16_t* As = ST == 0 ? A0 : A1;
+    const uint16_t* Bs = ST == 0 ? B0 : B1;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this step's loads are in LDS
+    __syncthreads();                                   // everyone's are; stage ST^1 is free
+    if constexpr (NEXT) issue(std::integral_constant<int, ST ^ 1>{}, (s + 1) * kBK);
+    const uint16_t* Ab = As + (wm * WR + (lane & 31)) * kBK;
+    const uint16_t* Bb = Bs + (wn * 64 + (lane & 31)) * kBK;
+    bf16x8_t af[2][I], bfr[2][J];
+    auto load_frags = [&](int kk, int slot) {
+      const int off = ((kk * 2 + hi) ^ sw) * kChunkBf16;
+#pragma unroll
+      for (int i = 0; i < I; ++i) af[slot][i] = *(const bf16x8_t*)(Ab + i * 32 * kBK + off);
+#pragma unroll
+      for (int j = 0; j < J; ++j) bfr[slot][j] = *(const bf16x8_t*)(Bb + j * 32 * kBK + off);
+    };
+    auto mfmas = [&](int slot) {
+#pragma unroll
+      for (int i = 0; i < I; ++i)
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[slot][i], bfr[slot][j], acc[i][j],
+                                                              0, 0, 0);
+    };
+    // fragments double-buffered across the four 16-wide k slices; the fences keep the
+    // compiler from hoisting all of a step's reads (and their registers) to its start
+    load_frags(0, 0);
+    load_frags(1, 1);
+    mfmas(0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags(2, 0);
+    mfmas(1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags(3, 1);
+    mfmas(0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(1);
+  };
+  using yes = std::true_type;
+  using no = std::false_type;
+  using st0 = std::integral_constant<int, 0>;
+  using st1 = std::integral_constant<int, 1>;
+  // steps run in pairs so each stage is static, and the last pair is peeled, so there
+  // is no branch between loop and epilogue (an odd tail merged there made the compiler
+  // shuffle the accumulators through scratch): hence K % 128 == 0
+  const int steps = K / kBK;
+  issue(st0{}, 0);
+  int s = 0;
+  for (; s + 2 < steps; s += 2) {
+    step(s, st0{}, yes{});
+    step(s + 1, st1{}, yes{});
+  }
+  step(s, st0{}, yes{});
+  step(s + 1, st1{}, no{});
+
+#pragma unroll
+  for (int i = 0; i < I; ++i)
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = wm * WR + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+        const int col = n0 + wn * 64 + j * 32 + (lane & 31);
+        if (row < nrows)
+          y[(int64_t)(r0 + row) * Nout + col] = __builtin_bit_cast(uint16_t, (__bf16)acc[i][j][v]);
+      }
+}
+
+// Workgroup -> (tile, column block) for the direct body: the column blocks of one tile
+// run on one XCD and consecutive tiles on consecutive XCDs (workgroups are handed to the
+// 8 XCDs round-robin), so a tile's x rows are fetched into one L2 and shared by its
+// column blocks.  The grid covers the tile count rounded up to 8; workgroups past
+// max_tiles exit.  Measured against the row-tile-major order of the register-staged
+// body (same run): Zipf 925 -> 952 TFLOP/s, uniform 904 -> 952, 64 experts x 1024 rows
+// (K 2048 -> 1024) 833 -> 899, 8 x 4096 rows (K 4096 -> 1024) 878 -> 865.  Contiguous
+// tile ranges per XCD did no better, and ranges cut from the host's max_tiles bound
+// (which exceeds the real count) left the last XCDs idle: 833 on Zipf.
+template <int BN>
+__global__ __launch_bounds__(2 * BN) void grouped_gemm_direct_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, const uint16_t* __restrict__ wgt, int32_t G,
+    int32_t K, int32_t Nout, const int32_t* __restrict__ tile_expert,
+    const int32_t* __restrict__ tile_row0, const int32_t* __restrict__ tile_rows,
+    int32_t max_tiles, uint16_t* __restrict__ y) {
+  __shared__ __attribute__((aligned(16))) uint16_t A0[kMaxBM * kBK];
+  __shared__ __attribute__((aligned(16))) uint16_t A1[kMaxBM * kBK];
+  __shared__ __attribute__((aligned(16))) uint16_t B0[BN * kBK];
+  __shared__ __attribute__((aligned(16))) uint16_t B1[BN * kBK];
+  const int nblk = Nout / BN;
+  const int xcd = blockIdx.x & 7;
+  const int l = blockIdx.x >> 3;
+  const int tile = (l / nblk) * 8 + xcd;
+  const int jblk = l - (l / nblk) * nblk;
+  if (tile >= max_tiles) return;
+  // the same uniform exits and clipping as grouped_gemm_kernel
+  const int e = tile_expert[tile];
+  if (e < 0 || e >= G) return;
+  const int r0 = tile_row0[tile];
+  if (r0 < 0 || r0 >= rows) return;
+  const int nrows = (int)min((int64_t)min(tile_rows[tile], kMaxBM), rows - r0);
+  if (nrows < 1) return;
+  const int n0 = jblk * BN;
+  const uint16_t* wb = wgt + ((int64_t)e * Nout + n0) * K;
+  if (nrows > kMaxBM / 2)
+    gemm_tile_direct<kMaxBM, BN>(x, wb, K, Nout, r0, nrows, n0, A0, A1, B0, B1, y);
+  else
+    gemm_tile_direct<kMaxBM / 2, BN>(x, wb, K, Nout, r0, nrows, n0, A0, A1, B0, B1, y);
+}
+
 }  // namespace
 
 hipError_t launch_gemm_tiles(const int32_t* expert_offset, const int32_t* expert_count, int32_t G,
@@ -383,10 +574,22 @@ hipError_t launch_grouped_gemm(const uint16_t* x, int64_t rows, const uint16_t* 
   // 25.0 us with 256-column blocks vs 19.8 with 128-column ones; 8 x 4096 rows, 4096 ->
   // 1024: 60 vs 54 us; but 64 x 8192 rows, 2048 -> 1024 (256 workgroups): 70 vs 81 us,
   // hence the switch at the CU count.
+  // With K % 128 == 0 the first two shapes run the direct-to-LDS body (identical
+  // outputs); the split shape always runs the register-staged one, which was faster
+  // there (16 x 760 rows: 21.7 vs 25.7 us).
   constexpr int64_t kCUs = 256;
   const int64_t grid256 = Nout % 256 == 0 ? (int64_t)max_tiles * (Nout / 256) : 0;
   const int64_t grid128 = (int64_t)max_tiles * (Nout / 128);
-  if (grid256 >= kCUs) {
+  const int64_t tiles8 = ((int64_t)max_tiles + 7) / 8 * 8;
+  if (K % (2 * kBK) == 0 && grid256 >= kCUs) {
+    hipLaunchKernelGGL((grouped_gemm_direct_kernel<256>), dim3((unsigned)(tiles8 * (Nout / 256))),
+                       dim3(512), 0, stream, x, rows, w, G, K, Nout, tile_expert, tile_row0,
+                       tile_rows, max_tiles, y);
+  } else if (K % (2 * kBK) == 0 && grid128 >= kCUs) {
+    hipLaunchKernelGGL((grouped_gemm_direct_kernel<128>), dim3((unsigned)(tiles8 * (Nout / 128))),
+                       dim3(256), 0, stream, x, rows, w, G, K, Nout, tile_expert, tile_row0,
+                       tile_rows, max_tiles, y);
+  } else if (grid256 >= kCUs) {
     hipLaunchKernelGGL((grouped_gemm_kernel<256, false>), dim3((unsigned)grid256), dim3(512), 0,
                        stream, x, rows, w, G, K, Nout, tile_expert, tile_row0, tile_rows, y);
   } else if (grid128 >= kCUs) {

@@ -145,14 +145,17 @@ def _tiles_of(entries, size=None):
                            torch.tensor(cols[2], **i32), torch.tensor([len(entries)], **i32))
 
 
+@pytest.mark.parametrize("K", [64, 128])
 @pytest.mark.parametrize("size", [6, 260])
-def test_grouped_gemm_bad_tiles(gpu_lib, size):
+def test_grouped_gemm_bad_tiles(gpu_lib, size, K):
     """Hand-made tile arrays holding an expert id past G, a negative one, a first row
     past the end, a negative first row and a tile running past the last row: the bad
     tiles are skipped, the long one is clipped at the last row, the valid ones are
     computed, and rows no valid tile names keep their previous contents.  Six entries
-    launch the split shape (128-row halves), 260 the whole-tile shape (256-row body)."""
-    rows, K, Nout, G = 400, 64, 128, 3
+    launch the split shape (128-row halves), 260 the whole-tile shape (256-row body):
+    register-staged at K = 64, direct-to-LDS at K = 128 (whose grid, rounded up to a
+    multiple of 8 tiles, also has workgroups past the last entry)."""
+    rows, Nout, G = 400, 128, 3
     rng = np.random.default_rng(11)
     x = _bf16(rng, (rows, K))
     w = _bf16(rng, (G, Nout, K), scale=0.1)
@@ -178,15 +181,18 @@ def test_grouped_gemm_bad_tiles(gpu_lib, size):
     assert np.all(yh[128:190] == sentinel)
 
 
-def test_grouped_gemm_launch_shapes_agree(gpu_lib):
+@pytest.mark.parametrize("K", [192, 256])
+def test_grouped_gemm_launch_shapes_agree(gpu_lib, K):
     """The kernel has three launch shapes, chosen by how far the grid fills the chip:
     256-column blocks, 128-column blocks, and 128-column blocks with every tile split
     over two workgroups.  One problem, with experts whose row counts straddle the 128-
     and 256-row bodies, is driven through all three by sizing the tile arrays (the exact
     bound, 200 entries, 300 entries; unused entries carry expert -1): the outputs must
-    be identical bit for bit and within the oracle's bound."""
+    be identical bit for bit and within the oracle's bound.  At K = 256 the first two
+    shapes run the direct-to-LDS body and the split one the register-staged body, so
+    the two bodies are compared bit for bit too."""
     counts = [0, 1, 127, 128, 129, 300, 0, 5, 255, 256, 257, 33, 96, 97, 520]
-    G, K, Nout = len(counts), 192, 256
+    G, Nout = len(counts), 256
     idx = np.concatenate([np.full(c, e, np.int32) for e, c in enumerate(counts)]).reshape(-1, 1)
     rng = np.random.default_rng(5)
     idx = idx[rng.permutation(len(idx))]
