@@ -541,10 +541,9 @@ def bench_small(args, dev):
                 xz = torch.where(x == -32768, torch.zeros_like(x), x)
                 assert bool((y == xz).all().item()), f"M={M} {tag} {name}: y != x"
             if M == ms[0] and not dedup:
-                # average launch duration of each kernel over 50 back-to-back launches
-                # between two events (one launch of a kernel this short is mostly launch
-                # gap), for the roofline of whichever path is faster
-                stream = torch.cuda.current_stream()
+                # duration of each kernel, for the roofline of whichever form is faster:
+                # graph replay of the kernel alone (eager launches of a kernel this short
+                # measure the host's launch rate, not the kernel)
                 rb = w.row_bytes
                 kern = {
                     "layout": (lambda: moedl.moe_dispatch_layout(idx, ebkt, B, False, out=lay),
@@ -557,16 +556,7 @@ def bench_small(args, dev):
                                                                           lay=lay, out=out),
                                         (M + M * k) * rb),
                 }
-                kern_us = {}
-                for name, (fn, _) in kern.items():
-                    e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-                    fn()
-                    e[0].record(stream)
-                    for _ in range(50):
-                        fn()
-                    e[1].record(stream)
-                    torch.cuda.synchronize()
-                    kern_us[name] = e[0].elapsed_time(e[1]) * 1e3 / 50
+                kern_us = {name: graph_replay_us(torch, fn) for name, (fn, _) in kern.items()}
                 kern_bytes = {n: b for n, (_, b) in kern.items()}
         rows.append(res)
     head = rows[0]
@@ -576,7 +566,7 @@ def bench_small(args, dev):
     members = ["layout", "dispatch", "combine"] if best == "three_calls" else ["layout_dispatch", "combine"]
     dom = max(members, key=lambda n: kern_us[n])
     roofline = hbm_roofline(dom, kern_bytes[dom], kern_us[dom], M=head["M"],
-                            launch_us_back_to_back={n: round(v, 2) for n, v in kern_us.items()})
+                            graph_us_per_kernel={n: round(v, 2) for n, v in kern_us.items()})
     cpu = None if args.no_cpu else cpu_small_baseline(workloads.make_workload(1, M=ms[0]))
     out = {"metric": "small-M layout+dispatch+combine latency (graph replay, us per step)",
            "value": head[f"flat_{best}_graph_us"], "unit": "us", "n_gpus": 1, "steps": args.steps,
