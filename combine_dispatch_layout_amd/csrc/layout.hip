@@ -515,9 +515,10 @@ constexpr int kFusedPieceVecs = kTileThreads;  // 16-byte vectors per work item
 constexpr int kFusedBatch = 4;                  // work items loaded together
 // Grid cap: two workgroups per CU, which fit at once for every instantiation (41-68 KiB
 // of LDS each).  Every workgroup recomputes the layout before copying, so a grid that
-// does not fit at once pays that again in a second wave.  Measured (graph replay,
-// layout + dispatch + combine, N=7168, top-8): cap 256 / 512 / 1024 -> 27.4 / 23.1 /
-// 30.5 us at M=256, 47.6 / 38.4 / 51.7 us at M=512, equal at M <= 128.
+// does not fit at once pays that again in a second wave, while fewer workgroups give
+// the copies less parallelism.  Measured (graph replay, layout + dispatch + combine,
+// N=7168, top-8, dedup off): cap 128 / 256 / 512 / 1024 -> 25.5 / 22.5 / 22.5 / 28.1 us
+// at M=256, 45.8 / 36.9 / 36.2 / 46.1 us at M=512; dedup on alike.
 constexpr int kFusedMaxBlocks = 512;
 
 template <int KC, int NTILE, int NC>
