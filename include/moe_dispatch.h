@@ -350,8 +350,10 @@ moe_status moe_grouped_gemm_tiles(const int32_t* expert_offset, const int32_t* e
  *   most MOE_GEMM_TILE_M rows per tile gives the same y; rows of a tile past that many
  *   are not computed),
  *   y  bf16 [rows, Nout]; rows outside every tile are not written.
- *   Every element is the same whichever of the kernel's launch shapes runs: each output
- *   element is one lane's k-ordered fp32 accumulation.
+ *   Every element is the same whichever launch shape and kernel body run (operands
+ *   copied global -> LDS directly when K % 128 == 0 and the grid fills the chip, staged
+ *   through registers otherwise): each output element is one lane's k-ordered fp32
+ *   accumulation.
  * Errors: MOE_ERR_INVALID_ARGUMENT (null or misaligned pointers, sizes < 1),
  * MOE_ERR_UNSUPPORTED (K % 64 != 0, Nout % 128 != 0, MOE_GEMM_TILE_M * K * 2 > 2^31 - 1,
  * max_tiles * Nout / 128 > 2^23),
