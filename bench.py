@@ -225,7 +225,7 @@ def bench_bucket(args, w, dev):
     res = {"metric": METRIC + " [dedup round trip]", "value": round(total / (ms * 1e-3) / 1e9, 1),
            "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
            "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
-           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "vs_baseline": None, "dtype": "bf16 rows, f32 accumulation", "data": "synthetic",
            "config": {"workload": wl_name, "M": M, "N": N, "G": G, "k": k,
                       "B": B, "send_rows": R, "dedup_saving": round(1 - R / (M * k), 4)},
            "us_per_step": round(ms * 1e3, 2), "alg_bytes_per_step": total,
@@ -324,6 +324,7 @@ def bench_placement(args, w, dev):
     res = {"metric": "expert placement: dedup saving (fraction of token copies removed)",
            "value": saving["greedy"], "unit": "fraction", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "higher_is_better": True, "vs_baseline": None,
+           "dtype": "int32",
            "data": "synthetic", "config": {"workload": w.name, "M": M, "G": G, "k": k, "B": B},
            "send_rows": rows, "dedup_saving": saving, "dedup_saving_second_half": holdout,
            "pair_counts_us": round(counts_us, 2), "greedy_host_ms": round(greedy_ms, 3),
@@ -421,7 +422,8 @@ def bench_gemm(args, w, dev):
     res = {"metric": "grouped GEMM TFLOP/s over the per-expert layout (bf16 in/out, fp32 acc)",
            "value": round(tflops, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round((t_tiles + t_gemm) * 1e-3, 4),
-           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16 operands, f32 accumulation",
            "data": "synthetic",
            "config": {"workload": wl_name, "rows": M * k, "K": N, "Nout": Nout, "G": G},
            "roofline": {"bound": "mfma", "achieved": round(tflops, 1),
@@ -571,7 +573,7 @@ def bench_small(args, dev):
     out = {"metric": "small-M layout+dispatch+combine latency (graph replay, us per step)",
            "value": head[f"flat_{best}_graph_us"], "unit": "us", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "higher_is_better": False, "scaling": "weak",
-           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "vs_baseline": None, "dtype": "bf16 rows, f32 accumulation", "data": "synthetic",
            "config": {"workload": "uniform-top8-N7168-G256-B8", "M": [r["M"] for r in rows],
                       "value_at": {"M": head["M"], "dedup": False, "form": best}},
            "roofline": roofline, "cpu_baseline": cpu, "rows": rows}
@@ -788,7 +790,8 @@ def main():
         "metric": METRIC, "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16" if not fp8 else "fp8_e4m3 rows, bf16 combine", "data": "synthetic",
+        "dtype": ("bf16 rows, f32 accumulation" if not fp8 else
+                  "fp8_e4m3 rows + f32 scales, f32 accumulation, bf16 out"), "data": "synthetic",
         "config": {"workload": w.name + ("-dedup" if dedup else ""), "M": M, "N": N, "G": G,
                    "k": k, "B": B, "dtype": w.dtype, "experts": w.standin, "dedup": dedup,
                    "send_rows": R, "parallelism": "single-gpu"},
