@@ -397,6 +397,8 @@ __device__ __forceinline__ void gemm_tile_direct(
       (void*)(x + (int64_t)r0 * K), (short)0, nrows * K * 2, kBufferWord3);
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
       (void*)wb, (short)0, BN * K * 2, kBufferWord3);
+  (void)xr;  // the loads that use them exist in the device pass only
+  (void)wr;
   // wave w issues instructions q = w, w + NWV, ...; lane L of instruction q loads row
   // 8 q + L / 8, global chunk (L % 8) ^ swizzle: byte offsets at k = 0
   const int lr = lane >> 3, pos = lane & 7;

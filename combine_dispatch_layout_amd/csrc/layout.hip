@@ -326,6 +326,8 @@ __device__ void expert_order_offsets(OrderLds<NT>& lds, const unsigned char* map
 
   // Contiguous maps (the bucket never decreases with the expert id; the common case)
   // order experts by id: the ranking is skipped and the counts are scanned in place.
+  // (One wave alone scanning the counts, with the map checked by a ballot in every wave
+  // and no barrier before it, measured 0.2 us slower at G = 256.)
   int mono = 1;
   for (int e = tid; e + 1 < G; e += NT) mono &= map_s[e] <= map_s[e + 1];
   if (__syncthreads_and(mono)) {
