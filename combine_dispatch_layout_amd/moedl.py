@@ -272,6 +272,8 @@ def moe_layout_dispatch(topk_idx: torch.Tensor, expert_bucket: torch.Tensor, B: 
     if x_scale is not None and out_scale is None:
         out_scale = torch.empty((rows, x_scale.shape[1]), dtype=torch.float32, device=x.device)
     sc = N // SCALE_BLOCK
+    # M comes from topk_idx, and the kernel reads M rows of x
+    _want(x, "x", _row_dtypes(x), M * N, cols=N)
     _want(out, "out", _row_dtypes(x), 0, cols=N)
     _want(x_scale, "x_scale", _F32, M * sc)
     _want(out_scale, "out_scale", _F32, out.shape[0] * sc)

@@ -39,6 +39,16 @@ def pair_counts(topk_idx: np.ndarray, G: int) -> np.ndarray:
     return S.T @ S
 
 
+def _visit_order(a_idx: np.ndarray, b_idx: np.ndarray, cnt: np.ndarray) -> np.ndarray:
+    """Step 2's visiting order of the pairs: count descending, then a, then b."""
+    return np.lexsort((b_idx, a_idx, -cnt))
+
+
+def _bucket_order(B: int):
+    """Steps 4 and 5 try the buckets lowest-numbered first."""
+    return range(B)
+
+
 def greedy_clusters(C: np.ndarray, cap: int) -> list[list[int]]:
     """Steps 1-2: clusters of at most `cap` experts, each a sorted member list, in
     step-3 order (size descending, then smallest member)."""
@@ -56,8 +66,7 @@ def greedy_clusters(C: np.ndarray, cap: int) -> list[list[int]]:
     cnt = C[a_idx, b_idx]
     keep = cnt > 0
     a_idx, b_idx, cnt = a_idx[keep], b_idx[keep], cnt[keep]
-    order = np.lexsort((b_idx, a_idx, -cnt))        # count desc, then a, then b
-    for p in order:
+    for p in _visit_order(a_idx, b_idx, cnt):
         ra, rb = find(int(a_idx[p])), find(int(b_idx[p]))
         if ra != rb and size[ra] + size[rb] <= cap:
             lo, hi = min(ra, rb), max(ra, rb)
@@ -80,7 +89,7 @@ def greedy_place(C: np.ndarray, B: int) -> np.ndarray:
     fill = [0] * B
     waiting = []
     for m in greedy_clusters(C, cap):
-        for b in range(B):
+        for b in _bucket_order(B):
             if fill[b] + len(m) <= cap:
                 bucket[m] = b
                 fill[b] += len(m)
@@ -89,7 +98,7 @@ def greedy_place(C: np.ndarray, B: int) -> np.ndarray:
             waiting.append(m)
     for m in waiting:
         for e in m:
-            b = next(b for b in range(B) if fill[b] < cap)
+            b = next(b for b in _bucket_order(B) if fill[b] < cap)
             bucket[e] = b
             fill[b] += 1
     return bucket

@@ -55,6 +55,21 @@ def test_dispatch_buffers(built_lib):
             x_scale=xs[:2])
 
 
+def test_layout_dispatch_rows_of_x(built_lib):
+    """The one-launch layout + dispatch takes M from topk_idx and reads M rows of x, so
+    an x with fewer rows is refused before any pointer is passed."""
+    M, N, k, G, B = 6, 256, 2, 16, 2
+    idx = torch.zeros((M, k), **i32)
+    ebkt = torch.zeros(G, **i32)
+    _raises(ValueError, "x: 256 elements, the call needs 1536", moedl.moe_layout_dispatch,
+            idx, ebkt, B, False, torch.zeros((1, N), dtype=torch.int16))
+    _raises(ValueError, "x: 768 elements", moedl.moe_layout_dispatch, idx, ebkt, B, True,
+            torch.zeros((3, N), dtype=torch.uint8))
+    # the right number of rows reaches the device check
+    _raises(ValueError, "must live on the GPU", moedl.moe_layout_dispatch, idx, ebkt, B,
+            False, torch.zeros((M, N), dtype=torch.int16))
+
+
 def test_combine_and_return_path(built_lib):
     M, k, N, rows = 5, 4, 64, 20
     eo = torch.zeros((rows, N), dtype=torch.int16)

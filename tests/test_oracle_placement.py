@@ -8,7 +8,9 @@
   counts above all inter-block ones) is recovered exactly; cluster partitions are
   equivariant under relabeling experts (tie-free counts); the 64 hot pairs of the
   correlated-pair workload stay together and the realised dedup saving beats
-  round-robin; planted mistakes fail a pin.
+  round-robin; hand-worked maps fix the tie order of the pair visits, the cluster
+  order and the bucket numbering (steps 2-5), and planted mistakes in each (ties by
+  (b, a), highest bucket first, clusters by smallest member) fail a pin.
 """
 import itertools
 
@@ -114,3 +116,99 @@ def test_planted_mistakes_fail_a_pin():
 
     m = ascending(C, 4)
     assert not all(len(set(m[g].tolist())) == 1 for g in groups)
+
+
+# ---- hand-worked maps: the tie order of step 2 and the bucket numbering of steps 4-5
+#
+# Each expected map below was derived by hand from the five steps, written out in the
+# comment, and not by running the oracle.
+
+def _sym(G, counts):
+    C = np.zeros((G, G), dtype=np.int64)
+    for (a, b), c in counts.items():
+        C[a, b] = C[b, a] = c
+    return C
+
+
+# G=6, B=2 (cap 3).  C[3,4]=10 merges {3,4}.  C[0,4] and C[1,3] tie at 5; visiting
+# (a, b) ascending takes (0,4) first: {0,3,4}, and (1,3) would make 4 > 3, so it is
+# skipped.  Clusters by size, then smallest member: [0,3,4], [1], [2], [5].  [0,3,4]
+# takes bucket 0 (full), the singletons fill bucket 1.  Visiting ties by (b, a) would
+# take (1,3) first and give [1,3,4] in bucket 0 instead.
+TIE_CASE = (_sym(6, {(3, 4): 10, (0, 4): 5, (1, 3): 5}), 2,
+            [[0, 3, 4], [1], [2], [5]], [0, 1, 1, 0, 0, 1])
+
+# G=8, B=2 (cap 4).  Merges {0,1} (count 3), {2,3} (2), then (3,4) makes {2,3,4}.
+# Order: [2,3,4] (size 3), [0,1], [5], [6], [7].  [2,3,4] -> bucket 0; [0,1] does not
+# fit there (3+2 > 4) -> bucket 1; [5] -> bucket 0 (now full); [6], [7] -> bucket 1.
+SIZE_CASE = (_sym(8, {(0, 1): 3, (2, 3): 2, (3, 4): 1}), 2,
+             [[2, 3, 4], [0, 1], [5], [6], [7]], [1, 1, 0, 0, 0, 0, 1, 1])
+
+# G=6, B=2 (cap 3).  Three pair clusters [0,1], [2,3], [4,5].  [0,1] -> bucket 0,
+# [2,3] -> bucket 1 (bucket 0 would hold 4), [4,5] fits nowhere and waits.  Step 5:
+# expert 4 takes the lowest bucket with a free place (0), then 5 takes bucket 1.
+WAIT_CASE = (_sym(6, {(0, 1): 3, (2, 3): 2, (4, 5): 1}), 2,
+             [[0, 1], [2, 3], [4, 5]], [0, 0, 1, 1, 0, 1])
+
+HAND_CASES = {"tie": TIE_CASE, "size": SIZE_CASE, "wait": WAIT_CASE}
+
+
+def _hand_pins_hold():
+    for C, B, clusters, m in HAND_CASES.values():
+        cap = C.shape[0] // B
+        if greedy_clusters(C, cap) != clusters:
+            return False
+        if greedy_place(C, B).tolist() != m:
+            return False
+    return True
+
+
+@pytest.mark.parametrize("case", sorted(HAND_CASES))
+def test_hand_worked_maps(case):
+    C, B, clusters, m = HAND_CASES[case]
+    assert greedy_clusters(C, C.shape[0] // B) == clusters
+    assert greedy_place(C, B).tolist() == m
+
+
+def test_hand_worked_maps_are_tie_sensitive():
+    """The tie case really is one: under the (b, a) order its clusters differ, so the
+    pin above decides between the two orders."""
+    C = TIE_CASE[0]
+    a_idx, b_idx = np.triu_indices(6, k=1)
+    cnt = C[a_idx, b_idx]
+    keep = cnt > 0
+    a_idx, b_idx, cnt = a_idx[keep], b_idx[keep], cnt[keep]
+    ab = [(int(a_idx[p]), int(b_idx[p])) for p in np.lexsort((b_idx, a_idx, -cnt))]
+    ba = [(int(a_idx[p]), int(b_idx[p])) for p in np.lexsort((a_idx, b_idx, -cnt))]
+    assert ab[:3] == [(3, 4), (0, 4), (1, 3)]
+    assert ba[:3] == [(3, 4), (1, 3), (0, 4)]
+
+
+def _mutant_ties_ba(a_idx, b_idx, cnt):
+    return np.lexsort((a_idx, b_idx, -cnt))         # ties by (b, a)
+
+
+def _mutant_highest_bucket(B):
+    return range(B - 1, -1, -1)                     # highest-numbered bucket first
+
+
+@pytest.mark.parametrize("name,mutant", [("_visit_order", _mutant_ties_ba),
+                                         ("_bucket_order", _mutant_highest_bucket)])
+def test_planted_tie_and_bucket_mistakes_fail_a_pin(monkeypatch, name, mutant):
+    import oracle.placement as pl
+    assert _hand_pins_hold()
+    monkeypatch.setattr(pl, name, mutant)
+    assert not _hand_pins_hold()
+
+
+def test_planted_cluster_order_mistake_fails_a_pin(monkeypatch):
+    """Step 3 taken as smallest member first (size ignored) changes the size case."""
+    import oracle.placement as pl
+    real = pl.greedy_clusters
+
+    def by_member(C, cap):
+        return sorted(real(C, cap), key=lambda m: m[0])
+
+    monkeypatch.setattr(pl, "greedy_clusters", by_member)
+    C, B, _, m = SIZE_CASE
+    assert pl.greedy_place(C, B).tolist() != m

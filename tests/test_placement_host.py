@@ -56,3 +56,12 @@ def test_errors():
     assert lib.moe_expert_pair_counts(1 << 20, 10, 8, 2048, 1 << 20, None) == 2
     assert lib.moe_expert_pair_counts(1 << 20, -1, 8, 64, 1 << 20, None) == 1
     assert lib.moe_expert_pair_counts(1 << 20, 10, 8, 64, None, None) == 1
+
+
+def test_hand_worked_maps():
+    """The host greedy gives the hand-derived maps that pin the oracle's tie order,
+    cluster order and bucket numbering."""
+    from test_oracle_placement import HAND_CASES
+    for C, B, _, m in HAND_CASES.values():
+        got = moedl.moe_place_experts(np.asarray(C, dtype=np.int32), B)
+        assert got.tolist() == m
