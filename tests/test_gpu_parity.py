@@ -102,33 +102,59 @@ def test_bench_workload_full_size(gpu_lib, cfg3, dedup):
     assert bool((y == x).all().item())
 
 
-def test_fp8_workload_full_size(gpu_lib):
-    """M=65536, fp8 e4m3 rows + fp32 per-128 scales, > 2^31-byte buffers."""
+def fp8_closed_form_check(w, y, chunk=8192):
+    """Every token of the fp8 workload, on the device: the stand-in experts all emit
+    e = bf16(f32(q) * s) for a token's row, and the token's weights sum to one within a
+    few fp32 ulps, so y must equal e bit for bit (a -0 comes back as +0): the
+    perturbation is far below half a bf16 ulp.  torch's own fp8 decode and RNE cast
+    compute e, independently of the library."""
+    xs = dev(w.x_scale)
+    x = dev(w.x)
+    for t0 in range(0, w.M, chunk):
+        t1 = min(w.M, t0 + chunk)
+        q = x[t0:t1].view(torch.float8_e4m3fn).float()
+        e = (q * xs[t0:t1].repeat_interleave(128, dim=1)).to(torch.bfloat16).view(torch.int16)
+        e = torch.where(e == -32768, torch.zeros_like(e), e)
+        bad = int((y[t0:t1] != e).sum().item())
+        assert bad == 0, f"{w.name}: {bad} elements of tokens [{t0}, {t1}) off the closed form"
+
+
+@pytest.mark.parametrize("dedup", [False, True])
+def test_fp8_workload_full_size(gpu_lib, dedup):
+    """M=65536, fp8 e4m3 rows + fp32 per-128 scales, > 2^31-byte buffers, both modes:
+    layout and dispatch compared in full, combine on sampled tokens against the oracle
+    and on every token against the closed form."""
     w = wl.make_workload(5)
-    say(f"full {w.name}")
-    ref = oracle.dispatch_layout(w.topk_idx, w.expert_bucket, w.B, False)
-    lay = gpu_layout(w, False)
+    say(f"full {w.name} dedup={dedup}")
+    ref = oracle.dispatch_layout(w.topk_idx, w.expert_bucket, w.B, dedup)
+    lay = gpu_layout(w, dedup)
     assert_layout_equal(lay, ref, w.name)
-    out, out_scale = gpu_dispatch(w, lay, sentinel=False)
+    out, out_scale = gpu_dispatch(w, lay, sentinel=dedup)
     assert_dispatch_equal(w, out, out_scale, ref, chunk=65536, ctx=w.name)
     eo = gpu_expert_outputs(w, lay, out, out_scale)
-    del out
+    del out, out_scale
     y = gpu_combine(w, lay, eo)
     torch.cuda.synchronize()
+    del eo
     rng = np.random.default_rng(5)
     tokens = np.sort(rng.choice(w.M, size=256, replace=False))
-    tokens[-1] = w.M - 1
+    tokens[0], tokens[-1] = 0, w.M - 1
     want = oracle_combine_tokens(w, ref, tokens)
     got = host(y[dev(tokens).long()])
+    assert max_rel_err(got, want) <= REL_TOL
     assert_bits_equal(got, want, w.name)
+    fp8_closed_form_check(w, y)
 
 
 @pytest.mark.parametrize("cfg,map_kind", [(2, "pair"), (4, "pair"), (4, "roundrobin")])
-def test_full_size_full_compare(gpu_lib, cfg, map_kind):
+@pytest.mark.parametrize("dedup", [False, True])
+def test_full_size_full_compare(gpu_lib, cfg, map_kind, dedup):
+    """Full size, every output compared, in the workload's quoted mode (dedup on) and
+    in the other one."""
     w = wl.make_workload(cfg, map_kind=map_kind)
-    say(f"full {w.name}")
-    ref, sent, sent_scale, eo_ref, y_ref = oracle_pipeline(w, w.dedup)
-    lay = gpu_layout(w, w.dedup)
+    say(f"full {w.name} dedup={dedup}")
+    ref, sent, sent_scale, eo_ref, y_ref = oracle_pipeline(w, dedup)
+    lay = gpu_layout(w, dedup)
     assert_layout_equal(lay, ref, w.name)
     out, out_scale = gpu_dispatch(w, lay)
     assert_dispatch_equal(w, out, out_scale, ref, ctx=w.name)
