@@ -7,7 +7,7 @@
 
 namespace {
 
-constexpr int32_t kAbiVersion = 2;
+constexpr int32_t kAbiVersion = 3;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 

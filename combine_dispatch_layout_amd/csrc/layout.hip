@@ -33,7 +33,10 @@
 //    launch.
 //  - M <= 512 with the row scatter in the same launch: layout_dispatch_small_kernel
 //    (every workgroup recomputes the layout in LDS, then copies its share of rows).
-//  - otherwise three launches, no inter-workgroup waiting and no initialised state:
+//  - 2 to kOnePassMaxTiles tiles (M <= 16384): layout_onepass_kernel, one launch.
+//    Each tile publishes its counts, waits (bounded) until every tile has, reduces
+//    the columns it needs itself and writes its slots from registers.
+//  - more tiles: three launches, no inter-workgroup waiting:
 //    layout_tile_kernel (per-tile ranks and totals to the workspace),
 //    layout_scan_kernel (one 1024-thread workgroup scans each expert / bucket column
 //    over tiles, orders experts, writes counts, offsets and the status word),
@@ -116,30 +119,45 @@ __device__ __forceinline__ int64_t wave_first_entry(int tile, int32_t k, int w) 
   return (int64_t)tile * kTileTokens * k + (int64_t)w * 64 * NC;
 }
 
-// Exclusive scan of src[0, n) into dst by one thread; dst[n] = the total when
-// with_total.  src may be dst.  For the short arrays here (n <= 64, usually a handful)
-// the independent LDS reads issue together, which beats a shuffle-based wave scan.
-// Callers put barriers around it.
-__device__ __forceinline__ void serial_exclusive_scan(const int32_t* src, int32_t* dst, int n,
-                                                      bool with_total) {
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int i = 0; i < n; ++i) {
-      const int v = src[i];
-      dst[i] = run;
-      run += v;
-    }
-    if (with_total) dst[n] = run;
+// Inclusive prefix sum over the 64 lanes of a wave with DPP (no LDS round trips):
+// shifts by 1, 2, 4 and 8 lanes inside each row of 16 (lanes shifted in from outside
+// the row read 0), then the last lane of rows 0 and 2 is added to rows 1 and 3
+// (row_bcast:15), and lane 31 to rows 2 and 3 (row_bcast:31).
+__device__ __forceinline__ int wave_inclusive_sum(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return x;
+}
+
+// Exclusive scan of src[0, n) into dst by one wave (n <= 64); dst[n] = the total when
+// with_total.  src may be dst (every lane reads before any writes).  Callers put
+// barriers around it.
+__device__ __forceinline__ void small_exclusive_scan(const int32_t* src, int32_t* dst, int n,
+                                                     bool with_total, int wave = 0) {
+  if ((int)(threadIdx.x >> 6) == wave) {
+    const int lane = threadIdx.x & 63;
+    const int v = lane < n ? src[lane] : 0;
+    const int incl = wave_inclusive_sum(v);
+    if (lane < n) dst[lane] = incl - v;
+    if (with_total && lane == 63) dst[n] = incl;
   }
 }
 
-template <int KC>  // KC: k rounded up to a power of two (chunks per wave)
+// A tile's tokens sit one per lane in its first kTokenWaves waves (the token view of
+// the dedup ranks); its (t, j) entries are spread over all NW waves of the workgroup.
+constexpr int kTokenWaves = kTileTokens / 64;
+
+template <int KC, int NW = kTileWaves>  // KC: k rounded up to a power of two
 struct TileLds {
   unsigned char map_s[kMaxE];
-  int32_t wcnt[kTileWaves][kMaxE];        // per-wave running counts, then prefixes
+  int32_t wcnt[NW][kMaxE];                // per-wave running counts, then prefixes
   int32_t ids_s[kTileTokens * KC];        // the tile's expert ids, flat order
-  uint64_t wbal[kTileWaves][kMaxB];       // dedup: per-wave ballot of each bucket
-  int32_t wbcnt[kTileWaves][kMaxB];       // dedup: per-wave counts, then prefixes
+  uint64_t wbal[kTokenWaves][kMaxB];      // dedup: per-wave ballot of each bucket
+  int32_t wbcnt[kTokenWaves][kMaxB];      // dedup: per-wave counts, then prefixes
   int32_t err_s;                          // first bad flat index in the tile
 };
 
@@ -150,18 +168,20 @@ __device__ __forceinline__ int64_t tile_end_entry(int32_t M, int32_t k, int tile
   return e < Mk ? e : Mk;
 }
 
-// Expert ranks of one 256-token tile, NC chunks per wave (see wave_first_entry).  On
-// return (after a barrier): ec[c] / rc[c] hold the expert id (or kAbsent) and the rank
-// inside the tile of flat entry wave_first_entry<NC>(tile, k, w) + c*64 + lane;
-// totals[e] holds the tile's count of expert e (totals may be global or LDS);
-// lds.ids_s holds the tile's ids (tile-local flat order) when keep_ids.
-template <int KC, int NC>
-__device__ __forceinline__ void tile_expert_ranks(TileLds<KC>& lds, const int32_t* __restrict__ idx,
+// Expert ranks of one 256-token tile, NW waves of NC chunks each (see
+// wave_first_entry; NW * NC = 4 * KC covers the tile).  On return (after a barrier):
+// ec[c] / rc[c] hold the expert id (or kAbsent) and the rank inside the tile of flat
+// entry wave_first_entry<NC>(tile, k, w) + c*64 + lane; totals[e] holds the tile's
+// count of expert e (totals may be global or LDS); lds.ids_s holds the tile's ids
+// (tile-local flat order) when keep_ids.
+template <int KC, int NC, int NW = kTileWaves>
+__device__ __forceinline__ void tile_expert_ranks(TileLds<KC, NW>& lds, const int32_t* __restrict__ idx,
                                                   int32_t M, int32_t k,
                                                   const int32_t* __restrict__ ebkt, int32_t G,
                                                   int32_t B, int tile, bool keep_ids,
                                                   int32_t* totals, int (&ec)[NC], int (&rc)[NC]) {
-  static_assert(NC <= KC, "a wave's chunks must fit the tile's id store");
+  static_assert(NC * NW <= KC * kTileWaves, "a wave's chunks must fit the tile's id store");
+  constexpr int NT = NW * 64;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = wave_index();
@@ -178,11 +198,11 @@ __device__ __forceinline__ void tile_expert_ranks(TileLds<KC>& lds, const int32_
     const int v = idx[valid ? f : 0];
     ec[c] = valid ? v : kAbsent;
   }
-  for (int e = tid; e < G; e += kTileThreads) {
+  for (int e = tid; e < G; e += NT) {
     const int b = ebkt[e];
     lds.map_s[e] = (b >= 0 && b < B) ? (unsigned char)b : kBadBucket;
 #pragma unroll
-    for (int ww = 0; ww < kTileWaves; ++ww) lds.wcnt[ww][e] = 0;
+    for (int ww = 0; ww < NW; ++ww) lds.wcnt[ww][e] = 0;
   }
   if (tid == 0) lds.err_s = kNoError;
   __syncthreads();
@@ -207,10 +227,10 @@ __device__ __forceinline__ void tile_expert_ranks(TileLds<KC>& lds, const int32_
   __syncthreads();
 
   // cross-wave exclusive prefix per expert; the column total is the tile's count
-  for (int e = tid; e < G; e += kTileThreads) {
+  for (int e = tid; e < G; e += NT) {
     int run = 0;
 #pragma unroll
-    for (int ww = 0; ww < kTileWaves; ++ww) {
+    for (int ww = 0; ww < NW; ++ww) {
       const int v = lds.wcnt[ww][e];
       lds.wcnt[ww][e] = run;
       run += v;
@@ -223,20 +243,22 @@ __device__ __forceinline__ void tile_expert_ranks(TileLds<KC>& lds, const int32_
     if (ec[c] >= 0) rc[c] += lds.wcnt[w][ec[c]];
 }
 
-// Dedup ranks of one tile (token view).  Needs lds.ids_s from tile_expert_ranks.  On
-// return (after a barrier): eb[j] is the bucket of token (lane)'s j-th entry or
+// Dedup ranks of one tile (token view: token w*64 + lane of the tile in waves w <
+// kTokenWaves; later waves hold no token).  Needs lds.ids_s from tile_expert_ranks.
+// On return (after a barrier): eb[j] is the bucket of the lane's token's j-th entry or
 // kBadBucket, dl[j] the token's rank among the tile's tokens that send to that
 // bucket; btotals[b] the tile's distinct-token count of bucket b.
-template <int KC>
-__device__ __forceinline__ void tile_dedup_ranks(TileLds<KC>& lds, int32_t M, int32_t k, int32_t B, int tile,
+template <int KC, int NW = kTileWaves>
+__device__ __forceinline__ void tile_dedup_ranks(TileLds<KC, NW>& lds, int32_t M, int32_t k, int32_t B, int tile,
                                  int32_t* btotals, int (&eb)[KC], int (&dl)[KC]) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = wave_index();
+  const bool token_wave = w < kTokenWaves;
   const uint64_t below = (1ull << lane) - 1ull;
   const int64_t t = (int64_t)tile * kTileTokens + (int64_t)w * 64 + lane;
-  const bool tv = t < M;
-  const int* my_ids = lds.ids_s + (w * 64 + lane) * k;
+  const bool tv = token_wave && t < M;
+  const int* my_ids = lds.ids_s + ((token_wave ? w * 64 : 0) + lane) * k;
   // Branch-free throughout: every LDS read is unconditional (clamped index, value
   // replaced afterwards), so the reads of all j are in flight together.
   int ev[KC];
@@ -255,7 +277,7 @@ __device__ __forceinline__ void tile_dedup_ranks(TileLds<KC>& lds, int32_t M, in
     const uint64_t bal = wave_ballot(tv && ((bmask >> b) & 1ull));
     mine = lane == b ? bal : mine;
   }
-  if (lane < B) {
+  if (token_wave && lane < B) {
     lds.wbal[w][lane] = mine;
     lds.wbcnt[w][lane] = __builtin_popcountll(mine);
   }
@@ -263,7 +285,7 @@ __device__ __forceinline__ void tile_dedup_ranks(TileLds<KC>& lds, int32_t M, in
   if (tid < B) {
     int run = 0;
 #pragma unroll
-    for (int ww = 0; ww < kTileWaves; ++ww) {
+    for (int ww = 0; ww < kTokenWaves; ++ww) {
       const int v = lds.wbcnt[ww][tid];
       lds.wbcnt[ww][tid] = run;
       run += v;
@@ -271,33 +293,31 @@ __device__ __forceinline__ void tile_dedup_ranks(TileLds<KC>& lds, int32_t M, in
     btotals[tid] = run;
   }
   __syncthreads();
+  const int wt = token_wave ? w : 0;  // waves without tokens read a valid row, unused
 #pragma unroll
   for (int j = 0; j < KC; ++j) {
     const int b = eb[j] != kBadBucket ? eb[j] : 0;
-    const int base = lds.wbcnt[w][b];
-    const uint64_t bal = lds.wbal[w][b];
+    const int base = lds.wbcnt[wt][b];
+    const uint64_t bal = lds.wbal[wt][b];
     dl[j] = eb[j] != kBadBucket ? base + __builtin_popcountll(bal & below) : -1;
   }
 }
 
-// Exclusive scan of one int per thread over an NT-thread workgroup.
+// Exclusive scan of one int per thread over an NT-thread workgroup: a DPP scan in
+// each wave, then every wave adds the totals of the waves before it (independent LDS
+// reads, no serial step).
 template <int NT>
 __device__ int block_exclusive_scan(int v, int32_t* wave_sums /* >= NT/64 */) {
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int o = __shfl_up(incl, d, 64);
-    if (lane >= d) incl += o;
-  }
+  const int incl = wave_inclusive_sum(v);
   if (lane == 63) wave_sums[w] = incl;
   __syncthreads();
-  serial_exclusive_scan(wave_sums, wave_sums, NT / 64, false);
-  __syncthreads();
-  const int r = wave_sums[w] + incl - v;
-  __syncthreads();
-  return r;
+  int base = 0;
+#pragma unroll
+  for (int q = 0; q < NT / 64; ++q) base += q < w ? wave_sums[q] : 0;
+  __syncthreads();  // wave_sums is reused by the next call
+  return base + incl - v;
 }
 
 // LDS for expert_order_offsets.
@@ -378,7 +398,7 @@ __device__ void expert_order_offsets(OrderLds<NT>& lds, const unsigned char* map
     lds.base[tid] = run;
   }
   __syncthreads();
-  serial_exclusive_scan(lds.base, lds.base, B, false);
+  small_exclusive_scan(lds.base, lds.base, B, false);
   __syncthreads();
   int pos[CH];
 #pragma unroll
@@ -456,7 +476,7 @@ __global__ __launch_bounds__(kTileThreads) void layout_single_kernel(
     btot_s[tid] = bsum_s[tid];
   }
   __syncthreads();
-  serial_exclusive_scan(btot_s, boff_s, B, true);
+  small_exclusive_scan(btot_s, boff_s, B, true);
   __syncthreads();
 
   for (int e = tid; e < G; e += kTileThreads) {
@@ -599,7 +619,7 @@ __global__ __launch_bounds__(kTileThreads) void layout_dispatch_small_kernel(
     btot_s[tid] = bt;
   }
   __syncthreads();
-  serial_exclusive_scan(btot_s, boff_s, B, true);
+  small_exclusive_scan(btot_s, boff_s, B, true);
   __syncthreads();
 
   if (writer) {
@@ -839,12 +859,7 @@ __global__ __launch_bounds__(kScanThreads) void layout_scan_kernel(
   }
   if (tid < 64) {  // bucket counts and their exclusive scan, one wave
     const int v = tid < B ? btot_s[tid] : 0;
-    int incl = v;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int o = __shfl_up(incl, d, 64);
-      if (tid >= d) incl += o;
-    }
+    const int incl = wave_inclusive_sum(v);
     if (tid < B) {
       bucket_count[tid] = v;
       bucket_offset[tid] = incl - v;
@@ -891,6 +906,329 @@ __global__ __launch_bounds__(256) void layout_finalize_kernel(
   if (r >= 0 && r < send_cap) send_token[r] = t;
 }
 
+// ------------------------------------------------- 2..kOnePassMaxTiles tiles, one launch
+// Every tile ranks its entries as layout_tile_kernel does and publishes one row of
+// counts (expert counts, then bucket counts in dedup mode) and an error word in the
+// region of this call, every value stored as value + 1 with agent-scope stores (sc1:
+// written through to the point where every XCD's loads see them).  The region is zero
+// before the call, so each word is its own flag: a tile reads all T rows with
+// agent-scope loads, polling (bounded) until every word it needs is nonzero, and sums
+// each column itself -- over the rows before it (its prefix) and over all rows (the
+// totals).  There is no arrival counter, no serial column scan and no second launch;
+// each tile orders the experts (identically) and writes its slots and send rows from
+// the ranks it still holds in registers.  Every tile is resident at once (T <=
+// kOnePassMaxTiles is far below one workgroup per CU), so the polls end as soon as the
+// slowest tile has published; a poll that expires anyway (about a second) makes the
+// status MOE_LAYOUT_STATUS_WAIT_EXPIRED, and every store stays in bounds regardless.
+//
+// Two regions alternate between calls: while a call publishes in one, its tiles clear
+// the rows the previous one-launch call published in the other (that call has ended,
+// so nobody reads them any more), each tile a share.  The last tile to leave (header
+// word 0) writes the status word, flips the region and records this call's rows for
+// the next call to clear.  The regions sit at fixed offsets, so calls of any size may
+// share a workspace; it must be zero-filled before its first use.
+constexpr int kSpinLimit = 1 << 20;  // polls (about 1 us each) before giving up
+constexpr int kRawBufferWord3 = 0x00020000;  // raw buffer resource: no format, no swizzle
+constexpr int kSc1 = 16;  // cache policy sc1: coherent across the XCDs' L2s
+
+__device__ __forceinline__ bool all_published(u32x4 v) {
+  return v[0] != 0u && v[1] != 0u && v[2] != 0u && v[3] != 0u;
+}
+
+// pre[c] = sum over rows t < tile and tot[c] = sum over all T rows of the Cp columns
+// (Cp % 4 == 0) of the row-major rows[T][Cp] (values stored + 1), into LDS, by an
+// NT-thread workgroup whose threads [T0, NT) read: 16-byte quads with agent-scope
+// buffer loads, PB at a time, reloading those not yet fully published.  (Threads
+// below T0 have stores in flight; a wave's loads complete only after its earlier
+// stores, so they take no part in the reads.)  When a row has fewer quads than there
+// are reading threads, `stride` groups of them take interleaved rows and seg_* (4 *
+// NT ints each) join the groups.  Returns false if some quad was still unpublished
+// when the poll gave up.
+template <int NT, int PB, int T0>
+__device__ __forceinline__ bool poll_column_sums(const int32_t* rows, int T, int Cp, int tile,
+                                                 int32_t* pre, int32_t* tot, int32_t* seg_pre,
+                                                 int32_t* seg_tot) {
+  constexpr int NP = NT - T0;  // reading threads
+  const int tid = threadIdx.x - T0;
+  const int Q = Cp / 4;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)rows, (short)0, T * Cp * 4, kRawBufferWord3);
+  const bool wide = Q >= NP;  // every reading thread owns whole columns
+  const int stride = wide ? 1 : NP / Q;
+  bool done = true;
+  for (int q0 = 0; q0 < Q; q0 += NP) {
+    const int q = wide ? q0 + tid : (tid >= 0 ? tid % Q : 0);
+    const int g = wide ? 0 : (tid >= 0 ? tid / Q : 0);
+    const bool active = tid >= 0 && (wide ? q < Q : g < stride);
+    u32x4 p = {0, 0, 0, 0}, a = {0, 0, 0, 0};
+    const int n = active ? (T - g + stride - 1) / stride : 0;  // rows g, g + stride, ...
+    for (int u0 = 0; u0 < n; u0 += PB) {
+      unsigned pend = 0;
+#pragma unroll
+      for (int i = 0; i < PB; ++i) pend |= (u0 + i < n ? 1u : 0u) << i;
+      for (int spin = 0; pend != 0u && spin < kSpinLimit; ++spin) {
+        u32x4 v[PB];
+#pragma unroll
+        for (int i = 0; i < PB; ++i) {
+          v[i] = u32x4{0, 0, 0, 0};
+          if ((pend >> i) & 1u)
+            v[i] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                           rs, ((g + (u0 + i) * stride) * Cp + 4 * q) * 4, 0, kSc1));
+        }
+#pragma unroll
+        for (int i = 0; i < PB; ++i) {
+          if (((pend >> i) & 1u) && all_published(v[i])) {
+            const u32x4 c = v[i] - 1u;
+            a += c;
+            if (g + (u0 + i) * stride < tile) p += c;
+            pend &= ~(1u << i);
+          }
+        }
+        if (pend != 0u) __builtin_amdgcn_s_sleep(1);
+      }
+      done = done && pend == 0u;
+    }
+    if (active) {
+      int32_t* dp = wide ? pre + 4 * q : seg_pre + g * Cp + 4 * q;
+      int32_t* dt = wide ? tot + 4 * q : seg_tot + g * Cp + 4 * q;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        dp[i] = (int)p[i];
+        dt[i] = (int)a[i];
+      }
+    }
+  }
+  __syncthreads();
+  if (!wide) {
+    for (int c = threadIdx.x; c < Cp; c += NT) {
+      int pp = 0, ss = 0;
+      for (int g = 0; g < stride; ++g) {
+        pp += seg_pre[g * Cp + c];
+        ss += seg_tot[g * Cp + c];
+      }
+      pre[c] = pp;
+      tot[c] = ss;
+    }
+    __syncthreads();
+  }
+  return done;
+}
+
+// Waves of the one-launch layout's workgroup: 16 (two 64-entry chunks per wave at
+// k = 8) when k > 2, else 4 * KC so that every wave holds at least one chunk.
+template <int KC>
+constexpr int onepass_waves() { return KC >= 4 ? 16 : 4 * KC; }
+
+template <int KC>
+__global__ __launch_bounds__(onepass_waves<KC>() * 64) void layout_onepass_kernel(
+    const int32_t* __restrict__ idx, int32_t M, int32_t k,
+    const int32_t* __restrict__ ebkt, int32_t G, int32_t B, int32_t dedup,
+    int32_t* __restrict__ expert_count, int32_t* __restrict__ expert_offset,
+    int32_t* __restrict__ bucket_count, int32_t* __restrict__ bucket_offset,
+    int32_t* __restrict__ slot, int32_t* __restrict__ send_row,
+    int32_t* __restrict__ send_token, int32_t* __restrict__ status, uint32_t* header,
+    int32_t* region0, int32_t* region1) {
+  constexpr int NW = onepass_waves<KC>();
+  constexpr int NT = NW * 64;
+  constexpr int NC = kTileWaves * KC / NW;  // chunks per wave
+  static_assert(NC >= 1 && NC * NW == kTileWaves * KC, "the waves cover the tile");
+  static_assert(8 * NT <= NW * kMaxE, "column-sum scratch fits the spent rank counters");
+  __shared__ TileLds<KC, NW> lds;
+  __shared__ OrderLds<NT> olds;
+  // a tile's row: expert counts [0, G), bucket counts [Gp, Gp + B) (dedup), zero pads
+  __shared__ int32_t pre_s[kRegionCols];
+  __shared__ int32_t tot_s[kRegionCols];
+  __shared__ int32_t off_s[kMaxE];
+  __shared__ int32_t bsum_s[kMaxB];
+  __shared__ int32_t boff_s[kMaxB + 1];
+  __shared__ int32_t err_s;
+  __shared__ int32_t mapbad_s;
+  __shared__ int32_t expired_s;
+  __shared__ int32_t sorted_map_s;
+
+  const int T = (int)gridDim.x;
+  const int tile = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = wave_index();
+  const int64_t Mk = (int64_t)M * k;
+  const int Gp = (G + 3) & ~3;
+  const int Cp = dedup ? Gp + ((B + 3) & ~3) : Gp;  // row pitch of this call, in ints
+  // which region this call publishes in, and what the previous call left in the other
+  const uint32_t parity = __hip_atomic_load(header + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 1u;
+  const int prev_T = (int)__hip_atomic_load(header + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int prev_Cp = (int)__hip_atomic_load(header + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  int32_t* const rows = parity ? region1 : region0;
+  int32_t* const old_rows = parity ? region0 : region1;
+  if (tid < kMaxB) bsum_s[tid] = 0;
+  if (tid == 0) {
+    err_s = kNoError;
+    mapbad_s = kNoError;
+    expired_s = 0;
+  }
+  for (int c = G + tid; c < Cp; c += NT) pre_s[c] = 0;  // pads (buckets below)
+
+  // this tile's ranks; its row (in pre_s until the column sums) goes to the region
+  int ec[NC], rc[NC];
+  tile_expert_ranks<KC, NC, NW>(lds, idx, M, k, ebkt, G, B, tile, dedup != 0, pre_s, ec, rc);
+  if (w == NW - 1) {  // is the map in range and nondecreasing in the expert id?
+    bool ok = true;
+#pragma unroll 4
+    for (int e = lane; e < G; e += 64) {
+      const int m = lds.map_s[e];
+      const int m1 = lds.map_s[e + 1 < G ? e + 1 : e];
+      ok &= (m != kBadBucket) & (m <= m1);
+    }
+    const bool sorted = wave_ballot(!ok) == 0;
+    if (lane == 0) sorted_map_s = sorted;  // read after the barriers below
+  }
+  int eb[KC], dl[KC];
+  if (dedup) tile_dedup_ranks<KC, NW>(lds, M, k, B, tile, pre_s + Gp, eb, dl);
+
+  // Wave 0 publishes (value + 1; nobody waits for these stores, readers poll the
+  // words) and then clears this tile's share of the previous call's rows; the other
+  // waves read.
+  if (w == 0) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(rows + (int64_t)tile * Cp), (short)0, Cp * 4, kRawBufferWord3);
+    for (int q = lane; q < Cp / 4; q += 64) {
+      const u32x4 v = {(uint32_t)pre_s[4 * q] + 1u, (uint32_t)pre_s[4 * q + 1] + 1u,
+                       (uint32_t)pre_s[4 * q + 2] + 1u, (uint32_t)pre_s[4 * q + 3] + 1u};
+      __builtin_amdgcn_raw_buffer_store_b128(v, rs, q * 16, 0, kSc1);
+    }
+    if (lane == 0)
+      __hip_atomic_store(rows + kRegionErrOffset + tile, (int32_t)((uint32_t)lds.err_s + 1u),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int64_t words = (int64_t)prev_T * prev_Cp;  // a multiple of 4
+    const int64_t q_lo = words / 4 * tile / T, q_hi = words / 4 * (tile + 1) / T;
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)old_rows, (short)0, (int)(words * 4), kRawBufferWord3);
+    for (int64_t q = q_lo + lane; q < q_hi; q += 64)
+      __builtin_amdgcn_raw_buffer_store_b128(u32x4{0, 0, 0, 0}, ro, (int)(q * 16), 0, kSc1);
+    if (tile == 0 && lane < prev_T)
+      __hip_atomic_store(old_rows + kRegionErrOffset + lane, 0, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();  // pre_s and the rank counters are overwritten below
+
+  // column sums over all tiles' rows: this tile's prefix and the totals (scratch: the
+  // per-wave rank counters, no longer needed).  The error words are polled too.
+  bool done = true;
+  if (w == 1 && lane < T) {
+    uint32_t e = 0;
+    for (int spin = 0; spin < kSpinLimit; ++spin) {
+      e = (uint32_t)__hip_atomic_load(rows + kRegionErrOffset + lane, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+      if (e != 0u) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    done = e != 0u;
+    if (done && (int)(e - 1u) != kNoError) atomicMin(&err_s, (int)(e - 1u));
+  }
+  constexpr int PB = KC >= 16 ? 4 : 8;  // quads polled at once (registers at k = 16)
+  done = poll_column_sums<NT, PB, 64>(rows, T, Cp, tile, pre_s, tot_s, &lds.wcnt[0][0],
+                                      &lds.wcnt[0][0] + 4 * NT) && done;
+  if (!done) expired_s = 1;  // read after the barriers below
+  const int32_t* bpre_s = pre_s + Gp;  // dedup: this tile's prefix of each bucket
+
+  // expert offsets in (bucket, id) order and bucket offsets (dedup: the bucket totals
+  // are columns Gp.. of the sums)
+  if (sorted_map_s) {
+    // (bucket, id) order is id order: wave 0 scans the counts (lane i holds a run of
+    // `per` consecutive experts); with dedup off each bucket starts at its first
+    // expert, so the bucket offsets fall out of the same scan.  With dedup, wave 1
+    // scans the distinct-token counts of the buckets.
+    if (w == 0) {
+      const int per = (G + 63) / 64;
+      int sum = 0;
+      for (int u = 0; u < per; ++u) {
+        const int e = lane * per + u;
+        sum += e < G ? tot_s[e] : 0;
+      }
+      int run = wave_inclusive_sum(sum) - sum;
+      for (int u = 0; u < per; ++u) {
+        const int e = lane * per + u;
+        if (e < G) {
+          off_s[e] = run;
+          if (!dedup) {  // buckets (map[e-1], map[e]] begin here; past the last, the end
+            const int b1 = lds.map_s[e];
+            for (int b = e == 0 ? 0 : lds.map_s[e - 1] + 1; b <= b1; ++b) boff_s[b] = run;
+            if (e == G - 1)
+              for (int b = b1 + 1; b <= B; ++b) boff_s[b] = run + tot_s[e];
+          }
+          run += tot_s[e];
+        }
+      }
+    }
+    if (dedup) small_exclusive_scan(tot_s + Gp, boff_s, B, true, 1);
+    __syncthreads();
+  } else {
+    for (int e = tid; e < G; e += NT) {
+      if (lds.map_s[e] == kBadBucket) atomicMin(&mapbad_s, e);
+      else atomicAdd(&bsum_s[lds.map_s[e]], tot_s[e]);
+    }
+    expert_order_offsets<NT>(olds, lds.map_s, tot_s, G, B, off_s);
+    small_exclusive_scan(dedup ? tot_s + Gp : bsum_s, boff_s, B, true);
+    __syncthreads();
+  }
+
+  if (tile == 0) {
+    for (int e = tid; e < G; e += NT) {
+      expert_count[e] = tot_s[e];
+      expert_offset[e] = off_s[e];
+    }
+    if (tid < B) bucket_count[tid] = boff_s[tid + 1] - boff_s[tid];
+    if (tid <= B) bucket_offset[tid] = boff_s[tid];
+  }
+
+  const int64_t wbase = wave_first_entry<NC>(tile, k, w);
+  const int64_t tend = tile_end_entry(M, k, tile);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int64_t f = wbase + (int64_t)c * 64 + lane;
+    if (f < tend) {
+      const int s = ec[c] >= 0 ? off_s[ec[c]] + pre_s[ec[c]] + rc[c] : -1;
+      slot[f] = s;
+      if (!dedup) {
+        send_row[f] = s;
+        if (s >= 0 && s < Mk) send_token[s] = (int)(f / k);
+      }
+    }
+  }
+  if (dedup && w < kTokenWaves) {
+    const int64_t t = (int64_t)tile * kTileTokens + (int64_t)w * 64 + lane;
+    const int64_t cap = (int64_t)M * (k < B ? k : B);
+    if (t < M) {
+#pragma unroll
+      for (int j = 0; j < KC; ++j) {
+        if (j < k) {
+          const int r = eb[j] != kBadBucket ? boff_s[eb[j]] + bpre_s[eb[j]] + dl[j] : -1;
+          send_row[t * k + j] = r;
+          if (r >= 0 && r < cap) send_token[r] = (int)t;
+        }
+      }
+    }
+  }
+
+  // leave: this tile's reads of the region are complete (consumed before the barriers
+  // above).  The count of tiles whose poll expired rides in the high half.
+  if (tid == 0) {
+    const uint32_t mine = 1u + (expired_s ? 0x10000u : 0u);
+    const uint32_t now =
+        __hip_atomic_fetch_add(header, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + mine;
+    if ((now & 0xFFFFu) == (uint32_t)T) {
+      status[0] = (now >> 16) ? MOE_LAYOUT_STATUS_WAIT_EXPIRED
+                  : mapbad_s != kNoError ? -(mapbad_s + 1)
+                  : (err_s != kNoError ? err_s + 1 : 0);
+      __hip_atomic_store(header + 1, parity ^ 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(header + 2, (uint32_t)T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(header + 3, (uint32_t)Cp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(header, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
 // Chunks of 64 entries per wave that cover one tile of `entries` entries with all
 // four waves (rounded up to a power of two by the callers' instantiations).
 inline int chunks_per_wave(int64_t entries) {
@@ -917,6 +1255,13 @@ void launch_tiles(const int32_t* topk_idx, int64_t M, int32_t k, const int32_t* 
     else if (nc <= 8 || KC == 8) MOEDL_SINGLE(KC >= 8 ? 8 : 1);
     else MOEDL_SINGLE(KC >= 16 ? 16 : 1);
 #undef MOEDL_SINGLE
+    return;
+  }
+  if (T >= 2 && T <= kOnePassMaxTiles) {  // (M = 0: no tiles, the scan kernel writes zeros)
+    hipLaunchKernelGGL(layout_onepass_kernel<KC>, dim3(T), dim3(onepass_waves<KC>() * 64), 0,
+                       stream, topk_idx, (int32_t)M, k, expert_bucket, G, B, dedup, expert_count,
+                       expert_offset, bucket_count, bucket_offset, slot, send_row, send_token,
+                       status, ws.header, ws.region[0], ws.region[1]);
     return;
   }
   if (T > 1) {
@@ -973,15 +1318,28 @@ hipError_t launch_fused(const int32_t* topk_idx, int64_t M, int32_t k, const int
 
 static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
+// [sync words | tile_hist | tile_bhist | tile_err], each part 256-byte aligned.
+// [header | region 0 | region 1 | tile_hist | tile_bhist | tile_err], each part
+// 256-byte aligned.  The regions (one-launch layout) sit at fixed offsets whatever the
+// sizes; the per-tile arrays of the three-launch layout follow only when it is used.
 size_t layout_workspace_bytes(int64_t M, int32_t G, int32_t B) {
   const size_t T = (size_t)layout_tiles(M);
-  return align256(T * G * 4) + align256(T * B * 4) + align256(T * 4) + 256;
+  size_t bytes = 256 + 2 * kRegionBytes;
+  if (T > (size_t)kOnePassMaxTiles || T == 0)
+    bytes += align256(T * G * 4) + align256(T * B * 4) + align256(T * 4);
+  return bytes;
 }
 
 LayoutWorkspace carve_layout_workspace(void* base, int64_t M, int32_t G, int32_t B) {
   const size_t T = (size_t)layout_tiles(M);
   char* p = (char*)base;
   LayoutWorkspace ws;
+  ws.header = (uint32_t*)p;
+  p += 256;
+  ws.region[0] = (int32_t*)p;
+  p += kRegionBytes;
+  ws.region[1] = (int32_t*)p;
+  p += kRegionBytes;
   ws.tile_hist = (int32_t*)p;
   p += align256(T * G * 4);
   ws.tile_bhist = (int32_t*)p;

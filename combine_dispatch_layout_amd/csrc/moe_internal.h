@@ -19,11 +19,31 @@ constexpr int kTileWaves = kTileThreads / 64;
 constexpr int kScanThreads = 1024;
 constexpr int kNoError = 0x7FFFFFFF;
 
+// Up to kOnePassMaxTiles tiles the layout is one launch: every tile publishes its
+// counts, waits (bounded) until all tiles have, and reduces the columns itself.
+constexpr int kOnePassMaxTiles = 64;
+
 struct LayoutWorkspace {
+  // one-launch layout (2..kOnePassMaxTiles tiles): a header of four words
+  //   [0] tiles that have left the current call   [1] region the next call publishes in
+  //   [2] tiles and [3] row pitch of the call that published last (its rows are
+  //       cleared by the next one-launch call)
+  // and two publication regions at fixed offsets, used by alternate calls.  Each
+  // region holds kOnePassMaxTiles rows of up to MOE_MAX_EXPERTS + MOE_MAX_BUCKETS
+  // counts, then one error word per tile, all stored as value + 1 so that zero means
+  // "not yet published".  Zero everywhere between calls, except the region of the
+  // last call.
+  uint32_t* header;
+  int32_t* region[2];
+  // three-launch layout (more tiles)
   int32_t* tile_hist;   // [T][G]: per-tile expert counts, then their column prefix
   int32_t* tile_bhist;  // [T][B]: per-tile distinct (token, bucket) counts, then prefix
   int32_t* tile_err;    // [T]:    first bad flat index in the tile, or kNoError
 };
+
+constexpr int kRegionCols = MOE_MAX_EXPERTS + MOE_MAX_BUCKETS;  // widest row, in ints
+constexpr int kRegionErrOffset = kOnePassMaxTiles * kRegionCols;  // error words, in ints
+constexpr size_t kRegionBytes = ((size_t)(kRegionErrOffset + kOnePassMaxTiles) * 4 + 255) & ~(size_t)255;
 
 inline int64_t layout_tiles(int64_t M) { return (M + kTileTokens - 1) / kTileTokens; }
 

@@ -190,7 +190,9 @@ def alloc_layout(M: int, k: int, G: int, B: int, dedup: bool, device="cuda") -> 
         slot=torch.empty((M, k), **i32), send_row=torch.empty((M, k), **i32),
         send_token=torch.empty(send_capacity(M, k, B, dedup), **i32),
         status=torch.empty(1, **i32),
-        workspace=torch.empty(max(1, workspace_bytes(M, k, G, B)), dtype=torch.uint8,
+        # zero-filled once: the layout's counters start at zero and every call
+        # leaves them there
+        workspace=torch.zeros(max(1, workspace_bytes(M, k, G, B)), dtype=torch.uint8,
                               device=device),
         dedup=dedup)
 

@@ -58,6 +58,11 @@ typedef enum moe_dtype {
 #define MOE_MAX_BUCKETS 64   /* B */
 #define MOE_SCALE_BLOCK 128  /* elements per fp32 scale */
 
+/* Status word of moe_dispatch_layout when the one-launch layout (2 to 64 tiles of
+ * 256 tokens) gave up waiting for its workgroups to be resident together (about a
+ * second); the other outputs are then unspecified but in bounds. */
+#define MOE_LAYOUT_STATUS_WAIT_EXPIRED (-2147483647 - 1)
+
 /* Version of this ABI (bumped on any signature change). */
 int32_t moe_abi_version(void);
 
@@ -66,9 +71,11 @@ const char* moe_status_string(moe_status status);
 
 /*
  * Bytes of device workspace moe_dispatch_layout needs for these sizes (a pure
- * host computation; 0 if the sizes are invalid).  The workspace holds per-tile
- * partial counts; it needs no initialisation and may be reused by any later call
- * on the same stream.
+ * host computation; 0 if the sizes are invalid).  The workspace holds two
+ * counters followed by per-tile partial counts.  It must be zero-filled once,
+ * before its first use (e.g. hipMemset after allocation); every call leaves the
+ * counters at zero again, so it may then be reused by any later call on the same
+ * stream, for any sizes it is large enough for.
  */
 size_t moe_dispatch_layout_workspace_bytes(int64_t M, int32_t k, int32_t G, int32_t B);
 
@@ -108,10 +115,12 @@ size_t moe_dispatch_layout_workspace_bytes(int64_t M, int32_t k, int32_t G, int3
  *                 Capacity M*k (dedup=0) or M*min(k, B) (dedup=1).
  *   status        int32 [1]: 0 when all ids are valid; t*k + j + 1 for the first
  *                 entry whose expert id is outside [0, G); -(e + 1) for the first
- *                 expert e whose bucket is outside [0, B) (checked first).
+ *                 expert e whose bucket is outside [0, B) (checked first);
+ *                 MOE_LAYOUT_STATUS_WAIT_EXPIRED (see above; checked before both).
  *   workspace     device scratch of at least
  *                 moe_dispatch_layout_workspace_bytes(M, k, G, B) bytes, 16-byte
- *                 aligned; overwritten.
+ *                 aligned, zero-filled before its first use; calls that overlap
+ *                 in time must not share it.
  * Errors: MOE_ERR_INVALID_ARGUMENT (M < 0, k < 1, k > G, G < 1, B < 1, a null
  * pointer for a non-empty array), MOE_ERR_UNSUPPORTED (G > 1024, k > 16, B > 64,
  * M*k >= 2^31), MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH.

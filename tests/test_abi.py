@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(header, loader):
 
 def test_version_and_strings():
     lib = moedl.load()
-    assert lib.moe_abi_version() == 2
+    assert lib.moe_abi_version() == 3
     assert lib.moe_status_string(0) == b"ok"
     assert lib.moe_status_string(3) == b"workspace too small"
 

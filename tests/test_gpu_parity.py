@@ -324,3 +324,27 @@ def test_concurrent_streams(gpu_lib):
         assert np.array_equal(host(lay.send_row), row_h)
         assert np.array_equal(host(out), out_h)
         assert np.array_equal(host(y), y_h)
+
+
+def test_workspace_shared_across_sizes_and_modes(gpu_lib):
+    """One zero-filled workspace serves a sequence of layouts of different sizes,
+    modes, expert counts and kernel paths (one launch for 2..64 tiles of 256 tokens,
+    three launches above, one tile below): each call clears what the previous
+    one-launch call published and publishes in the other region, so every result must
+    match the oracle bit for bit whatever came before it."""
+    seq = [(3, 16384, False), (2, 4096, True), (4, 16384, True), (3, 300, False),
+           (5, 65536, False), (2, 1000, False), (3, 100, True), (4, 8192, False),
+           (3, 16384, True), (2, 4096, False)]
+    ws_bytes = max(moedl.workspace_bytes(M, 8, wl.make_workload(c, M=M, with_rows=False).G, 8)
+                   for c, M, _ in seq)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")
+    for rep in range(2):
+        for cfg, M, dedup in seq:
+            w = wl.make_workload(cfg, M=M, with_rows=False)
+            ctx = f"{w.name} M={M} dedup={dedup} pass {rep}"
+            say(ctx)
+            lay = moedl.alloc_layout(w.M, w.k, w.G, w.B, dedup)
+            lay.workspace = ws
+            moedl.moe_dispatch_layout(dev(w.topk_idx), dev(w.expert_bucket), w.B, dedup, out=lay)
+            ref = oracle.dispatch_layout(w.topk_idx, w.expert_bucket, w.B, dedup)
+            assert_layout_equal(lay, ref, ctx)
