@@ -32,8 +32,8 @@ COMMON = [
 ]
 
 LIBS = {
-    "libmoedl.so": ["api.cpp", "layout.hip", "dispatch.hip", "combine.hip", "bucket.hip",
-                    "placement.hip", "gemm.hip"],
+    "libmoedl.so": ["api.cpp", "layout.hip", "noalloc.hip", "dispatch.hip", "combine.hip",
+                    "bucket.hip", "placement.hip", "gemm.hip"],
     "libmoedl_harness.so": ["harness.hip"],
 }
 

@@ -41,6 +41,9 @@ SIGNATURES = {
     "moe_dispatch_layout": (ctypes.c_int, [
         _i32p, _i64, _i32, _i32p, _i32, _i32, _i32, _i32p, _i32p, _i32p, _i32p, _i32p,
         _i32p, _i32p, _i32p, _vp, ctypes.c_size_t, _vp]),
+    "moe_dispatch_layout_noalloc": (ctypes.c_int, [
+        _i32p, _i64, _i32, _i32p, _i32, _i32, _i32, _i32p, _i32p, _i32p, _i32p, _i32p,
+        _i32p, _i32p, _i32p, _vp]),
     "moe_dispatch": (ctypes.c_int, [
         _vp, ctypes.c_int, _i64, _i32, _vp, _i32p, _i32, _i32, _vp, _vp, _i64, _vp]),
     "moe_layout_dispatch": (ctypes.c_int, [
@@ -215,6 +218,39 @@ def moe_dispatch_layout(topk_idx: torch.Tensor, expert_bucket: torch.Tensor, B: 
         _ptr(lay.slot), _ptr(lay.send_row), _ptr(lay.send_token), _ptr(lay.status),
         _ptr(lay.workspace), lay.workspace.numel(), _stream(stream, topk_idx))
     _check("moe_dispatch_layout", st)
+    return lay
+
+
+LAYOUT_SCRATCH_BYTES = 4 << 20  # the library's static workspace per GPU
+
+
+def moe_dispatch_layout_noalloc(topk_idx: torch.Tensor, expert_bucket: torch.Tensor, B: int,
+                                dedup: bool, out: Optional[Layout] = None,
+                                stream=None) -> Layout:
+    """moe_dispatch_layout with the library's static workspace (no workspace buffer).
+    The Layout's workspace field is an empty tensor."""
+    M, k = topk_idx.shape
+    G = expert_bucket.shape[0]
+    if topk_idx.dtype != torch.int32 or expert_bucket.dtype != torch.int32:
+        raise TypeError("topk_idx and expert_bucket must be int32")
+    if out is None:
+        i32 = dict(dtype=torch.int32, device=topk_idx.device)
+        lay = Layout(
+            expert_count=torch.empty(G, **i32), expert_offset=torch.empty(G, **i32),
+            bucket_count=torch.empty(B, **i32), bucket_offset=torch.empty(B + 1, **i32),
+            slot=torch.empty((M, k), **i32), send_row=torch.empty((M, k), **i32),
+            send_token=torch.empty(send_capacity(M, k, B, dedup), **i32),
+            status=torch.empty(1, **i32),
+            workspace=torch.empty(0, dtype=torch.uint8, device=topk_idx.device), dedup=dedup)
+    else:
+        lay = out
+        _check_layout(lay, M, k, G, B, dedup)
+    st = lib().moe_dispatch_layout_noalloc(
+        _ptr(topk_idx), M, k, _ptr(expert_bucket), G, B, int(dedup), _ptr(lay.expert_count),
+        _ptr(lay.expert_offset), _ptr(lay.bucket_count), _ptr(lay.bucket_offset),
+        _ptr(lay.slot), _ptr(lay.send_row), _ptr(lay.send_token), _ptr(lay.status),
+        _stream(stream, topk_idx))
+    _check("moe_dispatch_layout_noalloc", st)
     return lay
 
 

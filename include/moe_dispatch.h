@@ -134,6 +134,32 @@ moe_status moe_dispatch_layout(const int32_t* topk_idx, int64_t M, int32_t k,
                                size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * moe_dispatch_layout_noalloc -- moe_dispatch_layout with no workspace argument and
+ * no allocation, for callers that cannot allocate device memory: code under HIP
+ * graph capture, serving loops that must not call hipMalloc, harnesses that forbid
+ * it.
+ *
+ * Inputs, outputs, status word and errors are those of moe_dispatch_layout, and the
+ * results are identical.  The workspace is a static device array of
+ * MOE_LAYOUT_SCRATCH_BYTES that the library holds on each GPU it runs on until the
+ * process ends; sizes whose workspace query exceeds it are refused with
+ * MOE_ERR_WORKSPACE (every G, k and B up to 65,536 tokens fit; at G = 256, B = 8,
+ * about 850,000 tokens).  The call runs on the current device (`stream` must belong
+ * to it).  Every call on one GPU shares that GPU's array: calls that overlap in time
+ * race, calls ordered on a stream do not.  Nothing is allocated and no memset is
+ * issued; the array starts zero-filled and every call leaves it in that state.
+ */
+#define MOE_LAYOUT_SCRATCH_BYTES (4u << 20)
+
+moe_status moe_dispatch_layout_noalloc(const int32_t* topk_idx, int64_t M, int32_t k,
+                                       const int32_t* expert_bucket, int32_t G, int32_t B,
+                                       int32_t dedup, int32_t* expert_count,
+                                       int32_t* expert_offset, int32_t* bucket_count,
+                                       int32_t* bucket_offset, int32_t* slot,
+                                       int32_t* send_row, int32_t* send_token,
+                                       int32_t* status, hipStream_t stream);
+
+/*
  * moe_dispatch -- copy each token's row (and its scales) into its send rows.
  *
  * Passage: the gather of token rows into the destination-grouped send buffer, with

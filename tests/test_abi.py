@@ -219,3 +219,22 @@ def fused_call(idx=P, M=64, k=8, eb=P, G=256, B=8, dd=0, x=P, dtype=0, N=7168, x
 ])
 def test_layout_dispatch_argument_errors(kw, status):
     assert fused_call(**kw) == status
+
+
+def test_noalloc_layout_argument_errors():
+    """The no-allocation layout call checks like moe_dispatch_layout, and refuses sizes
+    whose workspace exceeds its static array, all before any HIP call."""
+    lib = moedl.load()
+
+    def call(M=100, k=8, G=256, B=8, dedup=0, idx=P, ptr=P):
+        return lib.moe_dispatch_layout_noalloc(idx, M, k, ptr, G, B, dedup, ptr, ptr, ptr, ptr,
+                                               ptr, ptr, ptr, ptr, None)
+
+    assert call(M=-1) == INVALID
+    assert call(k=0) == INVALID
+    assert call(k=9, G=8) == INVALID
+    assert call(dedup=2) == INVALID
+    assert call(G=2048) == UNSUPPORTED
+    assert call(idx=None) == INVALID
+    assert moedl.workspace_bytes(1 << 20, 8, 1024, 64) > moedl.LAYOUT_SCRATCH_BYTES
+    assert call(M=1 << 20, G=1024, B=64) == WORKSPACE
