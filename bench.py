@@ -21,6 +21,10 @@ oracle timed on the same inputs.
     python bench.py --path placement --cfg 4   # pair counts, greedy placement, savings
     python bench.py --path gemm      # tile metadata + MFMA grouped GEMM over the layout
     python bench.py --path small     # small M: fused layout+dispatch vs separate calls
+    python bench.py --path chain     # one layer in order: layout, dispatch, grouped GEMM
+                                     # (hidden -> hidden per expert), combine
+    python bench.py --path dispatch-x  # both dispatch shapes at a fixed 1.88 GB send
+                                       # buffer while x grows from 235 MB to 1.88 GB
 """
 from __future__ import annotations
 
@@ -60,12 +64,15 @@ def parse():
     ap.add_argument("--dedup", action="store_true", help="time dedup mode instead")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay leg")
-    ap.add_argument("--path", choices=["flat", "bucket", "placement", "gemm", "small"],
+    ap.add_argument("--path", choices=["flat", "bucket", "placement", "gemm", "small", "chain",
+                                       "dispatch-x"],
                     default="flat",
                     help="flat: layout+dispatch+combine; bucket: the dedup round trip; "
                          "placement: pair counts + greedy placement and their dedup savings; "
                          "gemm: grouped-GEMM tile metadata + the MFMA grouped GEMM; "
-                         "small: latency at M <= 512, fused layout+dispatch vs three calls")
+                         "small: latency at M <= 512, fused layout+dispatch vs three calls; "
+                         "chain: layout, dispatch, grouped GEMM (N -> N), combine in order; "
+                         "dispatch-x: dispatch shapes at a fixed send buffer, growing x")
     ap.add_argument("--nout", type=int, default=2048, help="grouped GEMM output width")
     ap.add_argument("--small-m", default="64,128,256,512",
                     help="token counts of the small path (comma-separated, each <= 512)")
@@ -439,6 +446,254 @@ def bench_gemm(args, w, dev):
     print(json.dumps(res))
 
 
+def bench_chain(args, w, dev):
+    """One MoE layer in the order it runs, on the headline routing: moe_dispatch_layout,
+    moe_dispatch, moe_grouped_gemm_tiles + moe_grouped_gemm (each expert's rows times its
+    own [N, N] bf16 weights, so the expert outputs have the hidden size and are the
+    combine's input, as the grouped-GEMM page places the GEMM between the two), and
+    moe_combine.  Per-kernel event times in that order, and beside them the same
+    dispatch and combine run back to back (identity experts), in the same process."""
+    import torch
+    from combine_dispatch_layout_amd import moedl
+    M, N, G, k, B = w.M, w.N, w.G, w.k, w.B
+    assert w.dtype == "bf16"
+    idx = torch.from_numpy(w.topk_idx).to(dev)
+    ebkt = torch.from_numpy(w.expert_bucket).to(dev)
+    x = torch.from_numpy(w.x.view(np.int16)).to(dev)
+    wts = torch.from_numpy(w.weights).to(dev)
+    rows = M * k
+    lay = moedl.alloc_layout(M, k, G, B, False, dev)
+    xe = torch.empty((rows, N), dtype=torch.int16, device=dev)
+    ye = torch.empty((rows, N), dtype=torch.int16, device=dev)
+    y = torch.empty((M, N), dtype=torch.int16, device=dev)
+    # expert weights N(0, 1/N): the outputs keep the inputs' scale
+    gen = torch.Generator(device=dev).manual_seed(13)
+    wt = torch.empty((G, N, N), dtype=torch.int16, device=dev)
+    for e in range(G):
+        wt[e] = (torch.randn((N, N), generator=gen, device=dev) * N ** -0.5).to(
+            torch.bfloat16).view(torch.int16)
+    moedl.moe_dispatch_layout(idx, ebkt, B, False, out=lay)
+    tiles = moedl.moe_grouped_gemm_tiles(lay.expert_offset, lay.expert_count, rows)
+
+    calls = [
+        ("layout", lambda: moedl.moe_dispatch_layout(idx, ebkt, B, False, out=lay)),
+        ("dispatch", lambda: moedl.moe_dispatch(x, lay.send_row, rows, out=xe)),
+        ("gemm_tiles", lambda: moedl.moe_grouped_gemm_tiles(lay.expert_offset, lay.expert_count,
+                                                             rows, out=tiles)),
+        ("grouped_gemm", lambda: moedl.moe_grouped_gemm(xe, wt, tiles, y=ye)),
+        ("combine", lambda: moedl.moe_combine(ye, wts, lay.slot, y=y)),
+    ]
+    y_flat = torch.empty_like(y)
+    flat = [calls[0], calls[1],
+            ("combine", lambda: moedl.moe_combine(xe, wts, lay.slot, y=y_flat))]
+
+    def timed(seq, steps, warmup):
+        for _ in range(max(1, warmup)):
+            for _, c in seq:
+                c()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(seq) + 1)]
+              for _ in range(steps)]
+        t0 = time.perf_counter()
+        for i in range(steps):
+            ev[i][0].record(stream)
+            for (_, c), e in zip(seq, ev[i][1:]):
+                c()
+                e.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        per = {n: float(np.mean([e[q].elapsed_time(e[q + 1]) for e in ev])) * 1e3
+               for q, (n, _) in enumerate(seq)}
+        return wall * 1e6 / steps, per
+
+    # the same chain with the dispatch shape of two waves per token (moe_dispatch's
+    # dedup flag selects it): after the GEMM's weight stream x is no longer in the
+    # last-level cache, where that shape holds up better
+    calls_2w = list(calls)
+    calls_2w[1] = ("dispatch", lambda: moedl.moe_dispatch(x, lay.send_row, rows, out=xe,
+                                                         dedup=True))
+    us_step, per = timed(calls, args.steps, args.warmup)
+    _, per_2w = timed(calls_2w, max(2, args.steps // 4), 1)
+    _, per_flat = timed(flat, args.steps, args.warmup)
+    for _, c in calls:  # the chain's outputs for the check below
+        c()
+    torch.cuda.synchronize()
+    assert int(lay.status.item()) == 0
+
+    # sanity on 8 sampled tokens: y[t] against float32 sums of the bf16 expert outputs
+    # (each a float32 mat-vec rounded once to bf16), within two bf16 roundings of the
+    # magnitude
+    for t in range(0, M, M // 8):
+        xt = x[t].view(torch.bfloat16).float()
+        ref = torch.zeros(N, device=dev)
+        mag = torch.zeros(N, device=dev)
+        for j in range(k):
+            o = (wt[int(idx[t, j])].view(torch.bfloat16).float() @ xt).to(torch.bfloat16).float()
+            ref += float(wts[t, j]) * o
+            mag += abs(float(wts[t, j])) * o.abs()
+        got = y[t].view(torch.bfloat16).float()
+        assert bool(((got - ref).abs() <= mag * 2.0 ** -6 + 1e-3).all().item()), "chain check"
+
+    flops = 2.0 * rows * N * N
+    gemm_tflops = flops / (per["grouped_gemm"] * 1e-6) / 1e12
+    row_bytes = N * 2
+    disp_bytes = (M + rows) * row_bytes
+    comb_bytes = (rows + M) * row_bytes
+    rates = {"dispatch_gbps": round(disp_bytes / (per["dispatch"] * 1e-6) / 1e9, 1),
+             "combine_gbps": round(comb_bytes / (per["combine"] * 1e-6) / 1e9, 1),
+             "grouped_gemm_tflops": round(gemm_tflops, 1)}
+    rates_flat = {"dispatch_gbps": round(disp_bytes / (per_flat["dispatch"] * 1e-6) / 1e9, 1),
+                  "combine_gbps": round(comb_bytes / (per_flat["combine"] * 1e-6) / 1e9, 1)}
+    wl_name = f"{w.name}-chain-K{N}-N{N}"
+    traffic = recorded_traffic("grouped_gemm", wl_name,
+                               os.path.join(PROFILES, f"hbm_traffic_{wl_name}.txt"))
+
+    # a 2 GiB plain copy: calibrates the HBM byte counters of a profiled run of this leg
+    from combine_dispatch_layout_amd import harness
+    src = torch.empty(1 << 30, dtype=torch.int16, device=dev)
+    dst = torch.empty_like(src)
+    harness.copy(src, dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+    cpu = None if args.no_cpu else cpu_chain_baseline(w, wt, lay)
+    res = {"metric": "MoE layer step in order (layout, dispatch, grouped GEMM N->N, combine), "
+                     "us per step, M=16384,N=7168,G=256,k=8",
+           "value": round(us_step, 1), "unit": "us", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(us_step * 1e-3, 4),
+           "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16 rows and weights, f32 accumulation", "data": "synthetic",
+           "config": {"workload": wl_name, "M": M, "N": N, "G": G, "k": k, "B": B,
+                      "rows": rows, "dedup": False},
+           "event_us": {n: round(v, 2) for n, v in per.items()},
+           "rates_in_chain": rates,
+           "event_us_two_wave_dispatch": {n: round(v, 2) for n, v in per_2w.items()},
+           "event_us_back_to_back": {n: round(v, 2) for n, v in per_flat.items()},
+           "rates_back_to_back": rates_flat,
+           "roofline": {"bound": "mfma", "kernel": "grouped_gemm", "achieved": round(gemm_tflops, 1),
+                        "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(gemm_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+                        "min_hbm_bytes_per_launch": int(G * N * N * 2 + 2 * rows * N * 2),
+                        "launch_us": round(per["grouped_gemm"], 2)},
+           "cpu_baseline": cpu}
+    print(json.dumps(res))
+
+
+def bench_dispatch_x(args, dev):
+    """moe_dispatch's two kernel shapes (k single-store waves; two waves sharing a
+    token's rows, which the call takes for dedup layouts) at one send-buffer size,
+    131,072 rows of N=7168 bf16 (1.88 GB), while the rows read grow: M=16384 tokens at
+    k=8, 32768 at k=4, 65536 at k=2, 131072 at k=1 (x from 235 MB to 1.88 GB), uniform
+    distinct routing over G=256 experts, 8 buckets.  Each launch follows a combine of
+    the dispatched rows, as in the step.  Separates the size of x (against the 256 MB
+    Infinity Cache) from the size of the send buffer."""
+    import torch
+    from combine_dispatch_layout_amd import moedl, workloads
+    N, G, B, R = 7168, 256, 8, 131072
+    rows = []
+    for k in (8, 4, 2, 1):
+        M = R // k
+        rng = np.random.default_rng([1234, 90, k])
+        idx = torch.from_numpy(workloads.uniform_topk(rng, M, G, k)).to(dev)
+        ebkt = torch.from_numpy(workloads.contiguous_buckets(G, B)).to(dev)
+        lay = moedl.moe_dispatch_layout(idx, ebkt, B, False)
+        gen = torch.Generator(device=dev).manual_seed(k)
+        x = torch.randn((M, N), generator=gen, device=dev).to(torch.bfloat16).view(torch.int16)
+        wts = torch.full((M, k), 1.0 / k, dtype=torch.float32, device=dev)
+        out = torch.empty((R, N), dtype=torch.int16, device=dev)
+        y = torch.empty((M, N), dtype=torch.int16, device=dev)
+        shapes = {"k_waves": False, "two_waves": True}
+        for flag in shapes.values():  # warm-up
+            moedl.moe_combine(out, wts, lay.slot, y=y)
+            moedl.moe_dispatch(x, lay.send_row, R, out=out, dedup=flag)
+        torch.cuda.synchronize()
+        ev = {n: [] for n in shapes}
+        for _ in range(max(4, args.steps // 10)):
+            for n, flag in shapes.items():
+                moedl.moe_combine(out, wts, lay.slot, y=y)
+                s_, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                s_.record()
+                moedl.moe_dispatch(x, lay.send_row, R, out=out, dedup=flag)
+                e_.record()
+                ev[n].append((s_, e_))
+        torch.cuda.synchronize()
+        st = lay.send_token
+        samp = torch.randint(0, R, (1024,), device=dev)
+        assert torch.equal(out[samp], x[st[samp].long()]), "dispatch check"
+        alg = (M + R) * N * 2
+        row = {"M": M, "k": k, "x_MB": round(M * N * 2 / 1e6), "send_MB": round(R * N * 2 / 1e6)}
+        for n in shapes:
+            us = float(np.median([s_.elapsed_time(e_) * 1e3 for s_, e_ in ev[n]]))
+            row[f"{n}_us"] = round(us, 1)
+            row[f"{n}_gbps"] = round(alg / us / 1e3, 1)
+        rows.append(row)
+        del out, x, y, lay, idx
+
+    # a 2 GiB plain copy: calibrates the HBM byte counters of a profiled run of this leg
+    from combine_dispatch_layout_amd import harness
+    src = torch.empty(1 << 30, dtype=torch.int16, device=dev)
+    dst = torch.empty_like(src)
+    harness.copy(src, dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+    worst = rows[-1]
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        Ms = 8192
+        w1 = workloads.make_custom(Ms, N, G, 1, B, seed=90)
+        lay_o = oracle.dispatch_layout(w1.topk_idx, w1.expert_bucket, B, False)
+        t0 = time.perf_counter()
+        oracle.dispatch(w1.x, lay_o.send_row, lay_o.R)
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(2 * Ms * N * 2 / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"dispatch of {Ms} tokens at k=1 ({dt:.3f} s), {host_cores()}"}
+    res = {"metric": "dispatch GB/s at a fixed 1.88 GB send buffer, x from 235 MB to 1.88 GB",
+           "value": worst["k_waves_gbps"], "unit": "GB/s", "n_gpus": 1,
+           "steps": max(4, args.steps // 10), "warmup": 1, "ms_per_step": round(worst["k_waves_us"] * 1e-3, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16 rows (byte copy)", "data": "synthetic",
+           "config": {"workload": "uniform-N7168-send131072-rows", "G": G, "B": B, "rows": R},
+           "cases": rows,
+           "roofline": hbm_roofline("dispatch", (worst["M"] + R) * N * 2, worst["k_waves_us"]),
+           "cpu_baseline": cpu}
+    print(json.dumps(res))
+
+
+def cpu_chain_baseline(w, wt, lay):
+    """The oracle on a bounded sample of the chain: layout, dispatch and combine of the
+    whole workload (single-threaded, as the flat leg), plus the oracle's grouped GEMM
+    (float64 products, one BLAS thread) on 64 rows of the busiest expert, extrapolated
+    to all rows by their FLOP count."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    base = cpu_baseline(w, False)
+    cnt = lay.expert_count.cpu().numpy()
+    e = int(np.argmax(cnt))
+    S = 64
+    lay_o = oracle.dispatch_layout(w.topk_idx, w.expert_bucket, w.B, False)
+    xe, _ = oracle.dispatch(w.x, lay_o.send_row, w.M * w.k)
+    r0 = int(lay_o.expert_offset[e])
+    x_s = np.ascontiguousarray(xe[r0:r0 + S])
+    del xe
+    w_s = wt[e:e + 1].cpu().numpy().view(np.uint16)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        oracle.grouped_gemm(x_s, w_s, np.array([0]), np.array([S]))
+        dt = time.perf_counter() - t0
+    gemm_s = dt * (w.M * w.k) / S
+    total = base["seconds"] + gemm_s
+    return {"value": round(total * 1e6, 0), "unit": "us", "cores": 1, "kind": "oracle",
+            "sample": (f"layout+dispatch+combine on all {w.M} tokens ({base['seconds']:.2f} s) "
+                       f"plus the grouped GEMM on {S} rows of expert {e} ({dt:.2f} s), "
+                       f"extrapolated by FLOP count to {w.M * w.k} rows ({gemm_s:.0f} s); "
+                       f"{host_cores()}"),
+            "seconds": round(total, 1)}
+
+
 def cpu_gemm_baseline(w, wt, Nout: int, sample_rows: int):
     """The oracle's grouped GEMM (float64 products), one BLAS thread, on the first
     `sample_rows` rows of the per-expert layout.  Its inputs come from the oracle's own
@@ -618,6 +873,9 @@ def main():
     if args.path == "small":
         bench_small(args, dev)
         return
+    if args.path == "dispatch-x":
+        bench_dispatch_x(args, dev)
+        return
     w = workloads.make_workload(args.cfg)
     if args.path == "bucket":
         bench_bucket(args, w, dev)
@@ -627,6 +885,9 @@ def main():
         return
     if args.path == "gemm":
         bench_gemm(args, w, dev)
+        return
+    if args.path == "chain":
+        bench_chain(args, w, dev)
         return
 
     M, N, G, k, B = w.M, w.N, w.G, w.k, w.B

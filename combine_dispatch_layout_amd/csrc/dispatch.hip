@@ -28,8 +28,8 @@
 // kernel runs the Zipf workload above in 313 instead of 323 us (6.74 TB/s, the
 // plain-copy ceiling) and correlated pairs (4 KiB rows) in 94 instead of 97 us.
 //
-// With a dedup layout (the caller says so), or a send buffer above 2 GiB, a second
-// shape is used, below.  Both shapes write the same bytes.
+// With a dedup layout (the caller says so), or rows x larger than the Infinity Cache
+// (k > 1), a second shape is used, below.  Both shapes write the same bytes.
 #include "moe_internal.h"
 
 namespace moedl {
@@ -137,14 +137,19 @@ hipError_t launch_dispatch(const void* x, int64_t M, int64_t row_bytes, const fl
   const int32_t pieces = (row_vecs + kPieceVecs - 1) / kPieceVecs;
   const int64_t blocks = M * pieces;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  // The k single-store waves shape is the faster one for send buffers up to 2 GiB
-  // (6.3-6.7 vs 5.8-6.1 TB/s from 0.5 to 2.11 GB, uniform and Zipf routing), but past
-  // 2 GiB it falls to ~3.7-3.8 TB/s (2.35, 2.82 and 3.76 GB send buffers, bf16 and fp8,
-  // with and without scales) while the shape of two waves sharing a token's rows holds
-  // ~5.2-5.5 TB/s (measured on MI355X; the store addresses are full 64-bit, so the cliff
-  // is the memory system's, not an offset's).  So large buffers take that shape too.
-  constexpr int64_t kSharedShapeBytes = (int64_t)2 << 30;
-  if (dedup || out_rows * row_bytes > kSharedShapeBytes) {
+  // The k single-store waves shape is the faster one while x fits the 256 MB Infinity
+  // Cache, where its loads return in ~840 cycles: 6.1-6.7 TB/s against 5.8 for two
+  // waves at x = 235 MB.  Once x outgrows it the loads take 1,500-2,600 cycles and a
+  // wave whose one store waits on one load loses most of its rate, while the shape of
+  // two waves sharing a token's rows (about four stores per load) holds up: at a fixed
+  // 1.88 GB send buffer, x = 470 MB (k = 4) runs at 4.1 vs 5.3 TB/s, x = 940 MB (k = 2)
+  // at 5.0 vs 5.6; at k = 1 the shapes are within 4% (5.65 vs 5.44).  The send-buffer
+  // size itself does not matter (1.88 GB written inside a 4 GiB allocation, or a 2.35
+  // GB buffer with x below the cache, behave like their x).  Measured on MI355X with
+  // EA read-latency counters (TCC_EA0_RDREQ_LEVEL / TCC_EA0_RDREQ); the threshold sits
+  // between x = 235 MB (k-wave faster) and 264 MB (two-wave faster).
+  constexpr int64_t kCacheResidentXBytes = (int64_t)240 << 20;
+  if (dedup || (k >= 2 && M * row_bytes > kCacheResidentXBytes)) {
 #define MOEDL_CASE(K)                                                                          \
   case K:                                                                                      \
     return launch_dedup_k<K>(x, M, row_vecs, pieces, x_scale, scale_cols, send_row, out,     \

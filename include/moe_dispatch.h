@@ -174,8 +174,8 @@ moe_status moe_dispatch_layout_noalloc(const int32_t* topk_idx, int64_t M, int32
  *   send_row  int32 [M*k] from moe_dispatch_layout (any map into rows works).
  *   dedup     0 or 1: whether send_row came from a dedup layout.  Only selects the
  *             kernel shape (k single-store waves per row piece, or two waves sharing
- *             the token's distinct rows; the latter also for send buffers above
- *             2 GiB); the bytes written are the same.
+ *             the token's distinct rows; the latter also when x is larger than the
+ *             GPU's last-level cache and k > 1); the bytes written are the same.
  * Outputs:
  *   out       [out_rows, N] elements of `dtype`; rows named by send_row are written.
  *   out_scale float [out_rows, N/128]; NULL exactly when x_scale is NULL.
