@@ -23,7 +23,7 @@ oracle timed on the same inputs.
     python bench.py --path small     # small M: fused layout+dispatch vs separate calls
     python bench.py --path chain     # one layer in order: layout, dispatch, grouped GEMM
                                      # (hidden -> hidden per expert), combine
-    python bench.py --path dispatch-x  # both dispatch shapes at a fixed 1.88 GB send
+    python bench.py --path dispatch-x  # dispatch (chosen shape, two-wave) at a fixed 1.88 GB send
                                        # buffer while x grows from 235 MB to 1.88 GB
 """
 from __future__ import annotations
@@ -581,13 +581,13 @@ def bench_chain(args, w, dev):
 
 
 def bench_dispatch_x(args, dev):
-    """moe_dispatch's two kernel shapes (k single-store waves; two waves sharing a
-    token's rows, which the call takes for dedup layouts) at one send-buffer size,
-    131,072 rows of N=7168 bf16 (1.88 GB), while the rows read grow: M=16384 tokens at
-    k=8, 32768 at k=4, 65536 at k=2, 131072 at k=1 (x from 235 MB to 1.88 GB), uniform
-    distinct routing over G=256 experts, 8 buckets.  Each launch follows a combine of
-    the dispatched rows, as in the step.  Separates the size of x (against the 256 MB
-    Infinity Cache) from the size of the send buffer."""
+    """moe_dispatch at one send-buffer size, 131,072 rows of N=7168 bf16 (1.88 GB),
+    while the rows read grow: M=16384 tokens at k=8, 32768 at k=4, 65536 at k=2, 131072
+    at k=1 (x from 235 MB to 1.88 GB), uniform distinct routing over G=256 experts, 8
+    buckets.  Two calls per case: `auto` (dedup=0: the call picks k single-store waves
+    while x fits the 256 MB Infinity Cache or k = 1, else two waves sharing a token's
+    rows) and `two_waves` (dedup=1: always the shared shape).  Each launch follows a
+    combine of the dispatched rows, as in the step."""
     import torch
     from combine_dispatch_layout_amd import moedl, workloads
     N, G, B, R = 7168, 256, 8, 131072
@@ -603,7 +603,7 @@ def bench_dispatch_x(args, dev):
         wts = torch.full((M, k), 1.0 / k, dtype=torch.float32, device=dev)
         out = torch.empty((R, N), dtype=torch.int16, device=dev)
         y = torch.empty((M, N), dtype=torch.int16, device=dev)
-        shapes = {"k_waves": False, "two_waves": True}
+        shapes = {"auto": False, "two_waves": True}
         for flag in shapes.values():  # warm-up
             moedl.moe_combine(out, wts, lay.slot, y=y)
             moedl.moe_dispatch(x, lay.send_row, R, out=out, dedup=flag)
@@ -652,13 +652,13 @@ def bench_dispatch_x(args, dev):
                "kind": "oracle",
                "sample": f"dispatch of {Ms} tokens at k=1 ({dt:.3f} s), {host_cores()}"}
     res = {"metric": "dispatch GB/s at a fixed 1.88 GB send buffer, x from 235 MB to 1.88 GB",
-           "value": worst["k_waves_gbps"], "unit": "GB/s", "n_gpus": 1,
-           "steps": max(4, args.steps // 10), "warmup": 1, "ms_per_step": round(worst["k_waves_us"] * 1e-3, 4),
+           "value": worst["auto_gbps"], "unit": "GB/s", "n_gpus": 1,
+           "steps": max(4, args.steps // 10), "warmup": 1, "ms_per_step": round(worst["auto_us"] * 1e-3, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": "bf16 rows (byte copy)", "data": "synthetic",
            "config": {"workload": "uniform-N7168-send131072-rows", "G": G, "B": B, "rows": R},
            "cases": rows,
-           "roofline": hbm_roofline("dispatch", (worst["M"] + R) * N * 2, worst["k_waves_us"]),
+           "roofline": hbm_roofline("dispatch", (worst["M"] + R) * N * 2, worst["auto_us"]),
            "cpu_baseline": cpu}
     print(json.dumps(res))
 
