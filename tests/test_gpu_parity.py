@@ -176,6 +176,8 @@ EDGE = [  # (M, N, G, k, B, dtype, routing, bucket_map)
     (333, 16, 64, 8, 8, "fp8", "uniform", "contiguous"),         # fp8, no scales
     (200, 8192, 128, 2, 2, "bf16", "uniform", "contiguous"),     # 16 KiB rows
     (90, 12288, 64, 3, 4, "bf16", "uniform", "contiguous"),      # rows above 16 KiB
+    (16384, 64, 1024, 16, 64, "bf16", "uniform", "random"),      # 64 tiles, one launch, max G, k, B
+    (16385, 64, 256, 8, 8, "bf16", "uniform", "random"),         # 65 tiles: three launches
 ]
 
 
