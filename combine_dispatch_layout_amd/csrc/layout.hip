@@ -35,7 +35,9 @@
 //    (every workgroup recomputes the layout in LDS, then copies its share of rows).
 //  - 2 to kOnePassMaxTiles tiles (M <= 16384): layout_onepass_kernel, one launch.
 //    Each tile publishes its counts, waits (bounded) until every tile has, reduces
-//    the columns it needs itself and writes its slots from registers.
+//    the columns it needs itself and writes its slots from registers.  Up to
+//    kOnePassMaxTiles tiles of 1024 tokens (M <= 65536, k <= 8) take the same kernel
+//    with 16 waves of one 64-token group each.
 //  - more tiles: three launches, no inter-workgroup waiting:
 //    layout_tile_kernel (per-tile ranks and totals to the workspace),
 //    layout_scan_kernel (one 1024-thread workgroup scans each expert / bucket column
@@ -114,9 +116,9 @@ __device__ __forceinline__ void stable_ranks(const bool (&ok)[C], const int (&ke
 // lane l being the entry at offset c * 64 + l.  NC = k rounded up to a power of two
 // covers a full tile; a single short tile (small M) takes the smallest NC that covers
 // it, so the work is spread over all waves with no idle chunks.
-template <int NC>
+template <int NC, int TT = kTileTokens>
 __device__ __forceinline__ int64_t wave_first_entry(int tile, int32_t k, int w) {
-  return (int64_t)tile * kTileTokens * k + (int64_t)w * 64 * NC;
+  return (int64_t)tile * TT * k + (int64_t)w * 64 * NC;
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave with DPP (no LDS round trips):
@@ -147,24 +149,25 @@ __device__ __forceinline__ void small_exclusive_scan(const int32_t* src, int32_t
   }
 }
 
-// A tile's tokens sit one per lane in its first kTokenWaves waves (the token view of
-// the dedup ranks); its (t, j) entries are spread over all NW waves of the workgroup.
-constexpr int kTokenWaves = kTileTokens / 64;
+// A tile of TT tokens (kTileTokens unless stated) has its tokens one per lane in its
+// first TT / 64 waves (the token view of the dedup ranks); its (t, j) entries are
+// spread over all NW waves of the workgroup.
 
-template <int KC, int NW = kTileWaves>  // KC: k rounded up to a power of two
+template <int KC, int NW = kTileWaves, int TT = kTileTokens>  // KC: k rounded up to a power of two
 struct TileLds {
   unsigned char map_s[kMaxE];
   int32_t wcnt[NW][kMaxE];                // per-wave running counts, then prefixes
-  int32_t ids_s[kTileTokens * KC];        // the tile's expert ids, flat order
-  uint64_t wbal[kTokenWaves][kMaxB];      // dedup: per-wave ballot of each bucket
-  int32_t wbcnt[kTokenWaves][kMaxB];      // dedup: per-wave counts, then prefixes
+  int32_t ids_s[TT * KC];                 // the tile's expert ids, flat order
+  uint64_t wbal[TT / 64][kMaxB];          // dedup: per-wave ballot of each bucket
+  int32_t wbcnt[TT / 64][kMaxB];          // dedup: per-wave counts, then prefixes
   int32_t err_s;                          // first bad flat index in the tile
 };
 
 // Last flat entry (exclusive) of a tile.
+template <int TT = kTileTokens>
 __device__ __forceinline__ int64_t tile_end_entry(int32_t M, int32_t k, int tile) {
   const int64_t Mk = (int64_t)M * k;
-  const int64_t e = ((int64_t)tile + 1) * kTileTokens * k;
+  const int64_t e = ((int64_t)tile + 1) * TT * k;
   return e < Mk ? e : Mk;
 }
 
@@ -174,20 +177,20 @@ __device__ __forceinline__ int64_t tile_end_entry(int32_t M, int32_t k, int tile
 // entry wave_first_entry<NC>(tile, k, w) + c*64 + lane; totals[e] holds the tile's
 // count of expert e (totals may be global or LDS); lds.ids_s holds the tile's ids
 // (tile-local flat order) when keep_ids.
-template <int KC, int NC, int NW = kTileWaves>
-__device__ __forceinline__ void tile_expert_ranks(TileLds<KC, NW>& lds, const int32_t* __restrict__ idx,
+template <int KC, int NC, int NW = kTileWaves, int TT = kTileTokens>
+__device__ __forceinline__ void tile_expert_ranks(TileLds<KC, NW, TT>& lds, const int32_t* __restrict__ idx,
                                                   int32_t M, int32_t k,
                                                   const int32_t* __restrict__ ebkt, int32_t G,
                                                   int32_t B, int tile, bool keep_ids,
                                                   int32_t* totals, int (&ec)[NC], int (&rc)[NC]) {
-  static_assert(NC * NW <= KC * kTileWaves, "a wave's chunks must fit the tile's id store");
+  static_assert(NC * NW <= KC * (TT / 64), "a wave's chunks must fit the tile's id store");
   constexpr int NT = NW * 64;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = wave_index();
   const int nbits = bits_for(G);
-  const int64_t wbase = wave_first_entry<NC>(tile, k, w);
-  const int64_t tend = tile_end_entry(M, k, tile);
+  const int64_t wbase = wave_first_entry<NC, TT>(tile, k, w);
+  const int64_t tend = tile_end_entry<TT>(M, k, tile);
   const int local0 = w * 64 * NC;  // tile-local index of the wave's first entry
 
   // all global loads first: clamped, unconditional, so they are in flight together
@@ -244,19 +247,21 @@ __device__ __forceinline__ void tile_expert_ranks(TileLds<KC, NW>& lds, const in
 }
 
 // Dedup ranks of one tile (token view: token w*64 + lane of the tile in waves w <
-// kTokenWaves; later waves hold no token).  Needs lds.ids_s from tile_expert_ranks.
+// TT / 64; later waves hold no token).  Needs lds.ids_s from tile_expert_ranks.
 // On return (after a barrier): eb[j] is the bucket of the lane's token's j-th entry or
 // kBadBucket, dl[j] the token's rank among the tile's tokens that send to that
 // bucket; btotals[b] the tile's distinct-token count of bucket b.
-template <int KC, int NW = kTileWaves>
-__device__ __forceinline__ void tile_dedup_ranks(TileLds<KC, NW>& lds, int32_t M, int32_t k, int32_t B, int tile,
+template <int KC, int NW = kTileWaves, int TT = kTileTokens>
+__device__ __forceinline__ void tile_dedup_ranks(TileLds<KC, NW, TT>& lds, int32_t M, int32_t k, int32_t B, int tile,
                                  int32_t* btotals, int (&eb)[KC], int (&dl)[KC]) {
+  constexpr int TW = TT / 64;  // token waves
+  static_assert(TW <= NW, "every token has a lane");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = wave_index();
-  const bool token_wave = w < kTokenWaves;
+  const bool token_wave = w < TW;
   const uint64_t below = (1ull << lane) - 1ull;
-  const int64_t t = (int64_t)tile * kTileTokens + (int64_t)w * 64 + lane;
+  const int64_t t = (int64_t)tile * TT + (int64_t)w * 64 + lane;
   const bool tv = token_wave && t < M;
   const int* my_ids = lds.ids_s + ((token_wave ? w * 64 : 0) + lane) * k;
   // Branch-free throughout: every LDS read is unconditional (clamped index, value
@@ -285,7 +290,7 @@ __device__ __forceinline__ void tile_dedup_ranks(TileLds<KC, NW>& lds, int32_t M
   if (tid < B) {
     int run = 0;
 #pragma unroll
-    for (int ww = 0; ww < kTokenWaves; ++ww) {
+    for (int ww = 0; ww < TW; ++ww) {
       const int v = lds.wbcnt[ww][tid];
       lds.wbcnt[ww][tid] = run;
       run += v;
@@ -928,6 +933,7 @@ __global__ __launch_bounds__(256) void layout_finalize_kernel(
 // the next call to clear.  The regions sit at fixed offsets, so calls of any size may
 // share a workspace; it must be zero-filled before its first use.
 constexpr int kSpinLimit = 1 << 20;  // polls (about 1 us each) before giving up
+constexpr int kWideTileTokens = 1024;  // tokens per tile above kOnePassMaxTiles 256-token tiles
 constexpr int kRawBufferWord3 = 0x00020000;  // raw buffer resource: no format, no swizzle
 constexpr int kSc1 = 16;  // cache policy sc1: coherent across the XCDs' L2s
 
@@ -1015,13 +1021,15 @@ __device__ __forceinline__ bool poll_column_sums(const int32_t* rows, int T, int
   return done;
 }
 
-// Waves of the one-launch layout's workgroup: 16 (two 64-entry chunks per wave at
-// k = 8) when k > 2, else 4 * KC so that every wave holds at least one chunk.
-template <int KC>
-constexpr int onepass_waves() { return KC >= 4 ? 16 : 4 * KC; }
+// Waves of the one-launch layout's workgroup.  Tiles of 256 tokens: 16 (two 64-entry
+// chunks per wave at k = 8) when k > 2, else 4 * KC so that every wave holds at least
+// one chunk.  Tiles of 1024 tokens (more than 64 tiles of 256): 16, one per 64 tokens,
+// KC chunks each.
+template <int KC, int TT = kTileTokens>
+constexpr int onepass_waves() { return TT > kTileTokens ? TT / 64 : (KC >= 4 ? 16 : 4 * KC); }
 
-template <int KC>
-__global__ __launch_bounds__(onepass_waves<KC>() * 64) void layout_onepass_kernel(
+template <int KC, int TT>
+__global__ __launch_bounds__((onepass_waves<KC, TT>() * 64)) void layout_onepass_kernel(
     const int32_t* __restrict__ idx, int32_t M, int32_t k,
     const int32_t* __restrict__ ebkt, int32_t G, int32_t B, int32_t dedup,
     int32_t* __restrict__ expert_count, int32_t* __restrict__ expert_offset,
@@ -1029,12 +1037,12 @@ __global__ __launch_bounds__(onepass_waves<KC>() * 64) void layout_onepass_kerne
     int32_t* __restrict__ slot, int32_t* __restrict__ send_row,
     int32_t* __restrict__ send_token, int32_t* __restrict__ status, uint32_t* header,
     int32_t* region0, int32_t* region1) {
-  constexpr int NW = onepass_waves<KC>();
+  constexpr int NW = onepass_waves<KC, TT>();
   constexpr int NT = NW * 64;
-  constexpr int NC = kTileWaves * KC / NW;  // chunks per wave
-  static_assert(NC >= 1 && NC * NW == kTileWaves * KC, "the waves cover the tile");
+  constexpr int NC = (TT / 64) * KC / NW;  // chunks per wave
+  static_assert(NC >= 1 && NC * NW == (TT / 64) * KC, "the waves cover the tile");
   static_assert(8 * NT <= NW * kMaxE, "column-sum scratch fits the spent rank counters");
-  __shared__ TileLds<KC, NW> lds;
+  __shared__ TileLds<KC, NW, TT> lds;
   __shared__ OrderLds<NT> olds;
   // a tile's row: expert counts [0, G), bucket counts [Gp, Gp + B) (dedup), zero pads
   __shared__ int32_t pre_s[kRegionCols];
@@ -1071,7 +1079,7 @@ __global__ __launch_bounds__(onepass_waves<KC>() * 64) void layout_onepass_kerne
 
   // this tile's ranks; its row (in pre_s until the column sums) goes to the region
   int ec[NC], rc[NC];
-  tile_expert_ranks<KC, NC, NW>(lds, idx, M, k, ebkt, G, B, tile, dedup != 0, pre_s, ec, rc);
+  tile_expert_ranks<KC, NC, NW, TT>(lds, idx, M, k, ebkt, G, B, tile, dedup != 0, pre_s, ec, rc);
   if (w == NW - 1) {  // is the map in range and nondecreasing in the expert id?
     bool ok = true;
 #pragma unroll 4
@@ -1084,7 +1092,7 @@ __global__ __launch_bounds__(onepass_waves<KC>() * 64) void layout_onepass_kerne
     if (lane == 0) sorted_map_s = sorted;  // read after the barriers below
   }
   int eb[KC], dl[KC];
-  if (dedup) tile_dedup_ranks<KC, NW>(lds, M, k, B, tile, pre_s + Gp, eb, dl);
+  if (dedup) tile_dedup_ranks<KC, NW, TT>(lds, M, k, B, tile, pre_s + Gp, eb, dl);
 
   // Wave 0 publishes (value + 1; nobody waits for these stores, readers poll the
   // words) and then clears this tile's share of the previous call's rows; the other
@@ -1126,7 +1134,7 @@ __global__ __launch_bounds__(onepass_waves<KC>() * 64) void layout_onepass_kerne
     done = e != 0u;
     if (done && (int)(e - 1u) != kNoError) atomicMin(&err_s, (int)(e - 1u));
   }
-  constexpr int PB = KC >= 16 ? 4 : 8;  // quads polled at once (registers at k = 16)
+  constexpr int PB = (KC >= 16 || TT > kTileTokens) ? 4 : 8;  // quads polled at once (registers)
   done = poll_column_sums<NT, PB, 64>(rows, T, Cp, tile, pre_s, tot_s, &lds.wcnt[0][0],
                                       &lds.wcnt[0][0] + 4 * NT) && done;
   if (!done) expired_s = 1;  // read after the barriers below
@@ -1182,8 +1190,8 @@ __global__ __launch_bounds__(onepass_waves<KC>() * 64) void layout_onepass_kerne
     if (tid <= B) bucket_offset[tid] = boff_s[tid];
   }
 
-  const int64_t wbase = wave_first_entry<NC>(tile, k, w);
-  const int64_t tend = tile_end_entry(M, k, tile);
+  const int64_t wbase = wave_first_entry<NC, TT>(tile, k, w);
+  const int64_t tend = tile_end_entry<TT>(M, k, tile);
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const int64_t f = wbase + (int64_t)c * 64 + lane;
@@ -1196,8 +1204,8 @@ __global__ __launch_bounds__(onepass_waves<KC>() * 64) void layout_onepass_kerne
       }
     }
   }
-  if (dedup && w < kTokenWaves) {
-    const int64_t t = (int64_t)tile * kTileTokens + (int64_t)w * 64 + lane;
+  if (dedup && w < TT / 64) {
+    const int64_t t = (int64_t)tile * TT + (int64_t)w * 64 + lane;
     const int64_t cap = (int64_t)M * (k < B ? k : B);
     if (t < M) {
 #pragma unroll
@@ -1258,11 +1266,25 @@ void launch_tiles(const int32_t* topk_idx, int64_t M, int32_t k, const int32_t* 
     return;
   }
   if (T >= 2 && T <= kOnePassMaxTiles) {  // (M = 0: no tiles, the scan kernel writes zeros)
-    hipLaunchKernelGGL(layout_onepass_kernel<KC>, dim3(T), dim3(onepass_waves<KC>() * 64), 0,
-                       stream, topk_idx, (int32_t)M, k, expert_bucket, G, B, dedup, expert_count,
-                       expert_offset, bucket_count, bucket_offset, slot, send_row, send_token,
-                       status, ws.header, ws.region[0], ws.region[1]);
+    hipLaunchKernelGGL((layout_onepass_kernel<KC, kTileTokens>), dim3(T),
+                       dim3(onepass_waves<KC, kTileTokens>() * 64), 0, stream, topk_idx,
+                       (int32_t)M, k, expert_bucket, G, B, dedup, expert_count, expert_offset,
+                       bucket_count, bucket_offset, slot, send_row, send_token, status,
+                       ws.header, ws.region[0], ws.region[1]);
     return;
+  }
+  // up to 64 tiles of 1024 tokens (M <= 65,536), k <= 8: the same single launch with
+  // four times the tokens per workgroup (k = 16 would not fit its ids in LDS)
+  const int64_t T4 = (M + kWideTileTokens - 1) / kWideTileTokens;
+  if constexpr (KC <= 8) {
+    if (T4 >= 2 && T4 <= kOnePassMaxTiles) {
+      hipLaunchKernelGGL((layout_onepass_kernel<KC, kWideTileTokens>), dim3((unsigned)T4),
+                         dim3(onepass_waves<KC, kWideTileTokens>() * 64), 0, stream, topk_idx,
+                         (int32_t)M, k, expert_bucket, G, B, dedup, expert_count, expert_offset,
+                         bucket_count, bucket_offset, slot, send_row, send_token, status,
+                         ws.header, ws.region[0], ws.region[1]);
+      return;
+    }
   }
   if (T > 1) {
     hipLaunchKernelGGL(layout_tile_kernel<KC>, dim3(T), dim3(kTileThreads), 0, stream, topk_idx,
