@@ -38,7 +38,8 @@
 //    the columns it needs itself and writes its slots from registers.  Up to
 //    kOnePassMaxTiles tiles of 1024 tokens (M <= 65536, k <= 8) take the same kernel
 //    with 16 waves of one 64-token group each.
-//  - more tiles: three launches, no inter-workgroup waiting:
+//  - more tiles (or k > 8 above 16384 tokens): three launches, no inter-workgroup
+//    waiting:
 //    layout_tile_kernel (per-tile ranks and totals to the workspace),
 //    layout_scan_kernel (one 1024-thread workgroup scans each expert / bucket column
 //    over tiles, orders experts, writes counts, offsets and the status word),

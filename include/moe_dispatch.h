@@ -59,8 +59,9 @@ typedef enum moe_dtype {
 #define MOE_SCALE_BLOCK 128  /* elements per fp32 scale */
 
 /* Status word of moe_dispatch_layout when the one-launch layout (2 to 64 tiles of
- * 256 tokens) gave up waiting for its workgroups to be resident together (about a
- * second); the other outputs are then unspecified but in bounds. */
+ * 256 tokens, or of 1024 tokens up to M = 65536 at k <= 8) gave up waiting for its
+ * workgroups to be resident together (about a second); the other outputs are then
+ * unspecified but in bounds. */
 #define MOE_LAYOUT_STATUS_WAIT_EXPIRED (-2147483647 - 1)
 
 /* Version of this ABI (bumped on any signature change). */

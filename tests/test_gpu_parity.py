@@ -177,7 +177,9 @@ EDGE = [  # (M, N, G, k, B, dtype, routing, bucket_map)
     (200, 8192, 128, 2, 2, "bf16", "uniform", "contiguous"),     # 16 KiB rows
     (90, 12288, 64, 3, 4, "bf16", "uniform", "contiguous"),      # rows above 16 KiB
     (16384, 64, 1024, 16, 64, "bf16", "uniform", "random"),      # 64 tiles, one launch, max G, k, B
-    (16385, 64, 256, 8, 8, "bf16", "uniform", "random"),         # 65 tiles: three launches
+    (16385, 64, 256, 8, 8, "bf16", "uniform", "random"),         # one launch, 1024-token tiles
+    (16385, 64, 256, 9, 8, "bf16", "uniform", "random"),         # k = 9 there: three launches
+    (65537, 16, 64, 2, 4, "bf16", "uniform", "random"),          # 65 tiles of 1024: three launches
 ]
 
 
@@ -330,13 +332,14 @@ def test_concurrent_streams(gpu_lib):
 
 def test_workspace_shared_across_sizes_and_modes(gpu_lib):
     """One zero-filled workspace serves a sequence of layouts of different sizes,
-    modes, expert counts and kernel paths (one launch for 2..64 tiles of 256 tokens,
-    three launches above, one tile below): each call clears what the previous
+    modes, expert counts and kernel paths (one launch for 2..64 tiles of 256 tokens
+    and, at k <= 8, up to 64 tiles of 1024; three launches above; one tile below):
+    each call clears what the previous
     one-launch call published and publishes in the other region, so every result must
     match the oracle bit for bit whatever came before it."""
     seq = [(3, 16384, False), (2, 4096, True), (4, 16384, True), (3, 300, False),
            (5, 65536, False), (2, 1000, False), (3, 100, True), (4, 8192, False),
-           (3, 16384, True), (2, 4096, False)]
+           (5, 70000, True), (3, 16384, True), (2, 4096, False)]
     ws_bytes = max(moedl.workspace_bytes(M, 8, wl.make_workload(c, M=M, with_rows=False).G, 8)
                    for c, M, _ in seq)
     ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")

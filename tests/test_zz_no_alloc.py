@@ -1,8 +1,8 @@
 """The no-allocation layout call (moe_dispatch_layout_noalloc, static device
 workspace) against moe_dispatch_layout with a caller workspace, through the C ABI:
 every output bit for bit, on two calls in a row with the second one smaller, for
-each kernel path (one launch for 2..64 tiles of 256 tokens, three launches above,
-one tile below) and both modes; then a longer mixed sequence that alternates the two
+each kernel path (one launch for 2..64 tiles of 256 tokens or, at k <= 8, of 1024
+tokens; three launches above; one tile below) and both modes; then a longer mixed sequence that alternates the two
 entry points, since the static array keeps each call's state for the next."""
 import numpy as np
 import pytest
@@ -36,7 +36,8 @@ def _assert_same(a, b, ctx):
 
 @pytest.mark.parametrize("first,second", [
     ((3, 16384), (2, 4096)),      # one launch, then one launch with fewer tiles
-    ((5, 65536), (3, 300)),       # three launches, then one launch with two tiles
+    ((5, 65536), (3, 300)),       # one launch of 1024-token tiles, then two tiles
+    ((5, 70000), (2, 4096)),      # three launches, then one launch
     ((4, 16384), (3, 200)),       # one launch (G=128), then a single tile
 ])
 @pytest.mark.parametrize("dedup", [False, True])
@@ -51,7 +52,8 @@ def test_noalloc_matches_workspace_call(gpu_lib, first, second, dedup):
 
 def test_noalloc_mixed_sequence(gpu_lib):
     seq = [(3, 16384, True), (2, 4096, False), (4, 8192, True), (5, 65536, True),
-           (3, 1000, False), (2, 100, True), (3, 16384, False), (4, 300, False)]
+           (5, 70000, False), (3, 1000, False), (2, 100, True), (3, 16384, False),
+           (4, 300, False)]
     for rep in range(2):
         for cfg, M, dedup in seq:
             w = wl.make_workload(cfg, M=M, with_rows=False)
