@@ -91,3 +91,19 @@ def test_committed_profiles_parse():
                 assert f"{kernel}.source_sha256:" in text
                 t = bench.recorded_traffic(kernel, wl, os.path.join(bench.PROFILES, name))
                 assert t is None or t > 0
+
+
+def test_event_steps():
+    """The timed loop records per-kernel events on a few evenly spaced steps: every step
+    when there are few of them, never one outside [0, K), and not the first step once
+    there are ten or more."""
+    assert bench.event_steps(3) == [0, 1, 2]
+    assert bench.event_steps(5) == [0, 1, 2, 3, 4]
+    assert bench.event_steps(20) == [2, 6, 10, 14, 18]
+    assert bench.event_steps(100) == [10, 30, 50, 70, 90]
+    for K in range(1, 300):
+        s = bench.event_steps(K)
+        assert all(0 <= i < K for i in s) and len(s) == min(K, 5)
+        assert s == sorted(set(s))
+        if K >= 10:
+            assert s[0] > 0
