@@ -172,10 +172,10 @@ __device__ __forceinline__ int64_t tile_end_entry(int32_t M, int32_t k, int tile
   return e < Mk ? e : Mk;
 }
 
-// Expert ranks of one 256-token tile, NW waves of NC chunks each (see
-// wave_first_entry; NW * NC = 4 * KC covers the tile).  On return (after a barrier):
-// ec[c] / rc[c] hold the expert id (or kAbsent) and the rank inside the tile of flat
-// entry wave_first_entry<NC>(tile, k, w) + c*64 + lane; totals[e] holds the tile's
+// Expert ranks of one tile of TT tokens (256 unless stated), NW waves of NC chunks
+// each (see wave_first_entry; NW * NC = (TT / 64) * KC covers the tile).  On return
+// (after a barrier): ec[c] / rc[c] hold the expert id (or kAbsent) and the rank inside
+// the tile of flat entry wave_first_entry<NC, TT>(tile, k, w) + c*64 + lane; totals[e] holds the tile's
 // count of expert e (totals may be global or LDS); lds.ids_s holds the tile's ids
 // (tile-local flat order) when keep_ids.
 template <int KC, int NC, int NW = kTileWaves, int TT = kTileTokens>
