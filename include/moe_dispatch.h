@@ -72,11 +72,13 @@ const char* moe_status_string(moe_status status);
 
 /*
  * Bytes of device workspace moe_dispatch_layout needs for these sizes (a pure
- * host computation; 0 if the sizes are invalid).  The workspace holds two
- * counters followed by per-tile partial counts.  It must be zero-filled once,
- * before its first use (e.g. hipMemset after allocation); every call leaves the
- * counters at zero again, so it may then be reused by any later call on the same
- * stream, for any sizes it is large enough for.
+ * host computation; 0 if the sizes are invalid).  The workspace holds a 256-byte
+ * header and the two publication regions of the one-launch layout at fixed offsets,
+ * then, for sizes that take the three-launch layout, per-tile partial counts.  It
+ * must be zero-filled once, before its first use (e.g. hipMemset after allocation);
+ * every call leaves it ready for the next one (the header and the region the next
+ * call publishes in are cleared), so it may then be reused by any later call on the
+ * same stream, for any sizes it is large enough for.
  */
 size_t moe_dispatch_layout_workspace_bytes(int64_t M, int32_t k, int32_t G, int32_t B);
 
