@@ -208,6 +208,60 @@ def test_edge_shapes(gpu_lib, case, dedup):
         assert_bits_equal(host(y), y_ref, ctx)
 
 
+def _random_cases(n=24, seed=20261203):
+    """Seeded random shapes across every layout path below 65,536 tokens (one tile,
+    one launch with 256- or 1024-token tiles), both row dtypes, repeats and all bucket
+    maps, bounded so that the oracle finishes each in well under a second."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        G = int(rng.choice([1, 3, 16, 64, 128, 256, 1000, 1024]))
+        k = int(rng.integers(1, min(16, G) + 1))
+        B = int(rng.integers(1, 65))
+        if rng.random() < 0.2:  # above 64 tiles of 256 tokens: the 1024-token tiles
+            k = min(k, 2)
+            M = int(rng.integers(16385, 40000 // k + 1))
+        else:
+            M = int(np.exp(rng.uniform(0, np.log(40000 // k))))
+        dtype = "fp8" if rng.random() < 0.25 else "bf16"
+        step = 16 if dtype == "fp8" else 8
+        N = int(rng.integers(1, 2048 // step + 1)) * step
+        if M * N * 2 > (32 << 20):
+            continue
+        routing = "repeats" if rng.random() < 0.3 else "uniform"
+        bmap = str(rng.choice(["contiguous", "random", "roundrobin"]))
+        dedup = bool(rng.random() < 0.5)
+        cases.append((M, N, G, k, B, dtype, routing, bmap, dedup))
+    return cases
+
+
+RANDOM = _random_cases()
+
+
+@pytest.mark.parametrize("case", RANDOM, ids=[
+    f"M{c[0]}-N{c[1]}-G{c[2]}-k{c[3]}-B{c[4]}-{c[5]}-{c[6]}-{c[7]}-{'dedup' if c[8] else 'flat'}"
+    for c in RANDOM])
+def test_random_shapes(gpu_lib, case):
+    M, N, G, k, B, dtype, routing, bmap, dedup = case
+    w = wl.make_custom(M, N, G, k, B, dtype=dtype, routing=routing, bucket_map=bmap, seed=M + N)
+    if dtype == "fp8":
+        w.x_scale = None
+    ctx = f"{w.name} map={bmap} dedup={dedup}"
+    say(ctx)
+    ref = oracle.dispatch_layout(w.topk_idx, w.expert_bucket, w.B, dedup)
+    lay = gpu_layout(w, dedup)
+    assert_layout_equal(lay, ref, ctx)
+    out, out_scale = gpu_dispatch(w, lay)
+    assert_dispatch_equal(w, out, out_scale, ref, ctx=ctx)
+    if dtype == "bf16":
+        sent, _ = oracle.dispatch(w.x, ref.send_row, ref.R)
+        eo_ref = oracle.expert_outputs("identity", sent, ref.send_row, ref.slot, w.topk_idx)
+        y_ref = oracle.combine(eo_ref, w.weights, ref.slot)
+        y = gpu_combine(w, lay, gpu_expert_outputs(w, lay, out, out_scale))
+        torch.cuda.synchronize()
+        assert_bits_equal(host(y), y_ref, ctx)
+
+
 def test_empty_batch(gpu_lib):
     from combine_dispatch_layout_amd import moedl
     idx = torch.empty((0, 8), dtype=torch.int32, device="cuda")
