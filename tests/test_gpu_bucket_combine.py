@@ -89,3 +89,35 @@ def test_single_bucket_matches_flat_combine(gpu_lib):
     y_flat = moedl.moe_combine(eo, dev(w.weights), lay.slot)
     torch.cuda.synchronize()
     assert torch.equal(y, y_flat)
+
+
+def _random_cases(n=12, seed=20261204):
+    """Seeded random shapes for the round trip (bf16 rows, scaled-expert stand-in), across
+    layout paths, repeats and all bucket maps; small enough for the oracle."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        G = int(rng.choice([1, 3, 16, 64, 256, 1000]))
+        k = int(rng.integers(1, min(16, G) + 1))
+        B = int(rng.integers(1, 65))
+        M = int(np.exp(rng.uniform(0, np.log(20000 // k))))
+        N = int(rng.integers(1, 1024 // 8 + 1)) * 8
+        if M * k * N * 2 > (24 << 20):
+            continue
+        routing = "repeats" if rng.random() < 0.3 else "uniform"
+        bmap = str(rng.choice(["contiguous", "random", "roundrobin"]))
+        cases.append((M, N, G, k, B, routing, bmap))
+    return cases
+
+
+RANDOM = _random_cases()
+
+
+@pytest.mark.parametrize("case", RANDOM, ids=[f"M{c[0]}-N{c[1]}-G{c[2]}-k{c[3]}-B{c[4]}-{c[5]}-{c[6]}"
+                                              for c in RANDOM])
+def test_round_trip_random(gpu_lib, case):
+    M, N, G, k, B, routing, bmap = case
+    w = wl.make_custom(M, N, G, k, B, routing=routing, bucket_map=bmap, seed=M + N + 11)
+    w.standin = "scale"
+    say(f"bucket round trip {w.name} map={bmap}")
+    check(w, f"{w.name} map={bmap}")

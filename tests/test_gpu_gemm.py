@@ -219,3 +219,45 @@ def test_grouped_gemm_launch_shapes_agree(gpu_lib, K):
     mag = magnitude(x, w, ref.expert_offset, ref.expert_count)
     got = oracle.bf16_to_f32(host(ys[0]).view(np.uint16)).astype(np.float64)
     _bound_check(got, exact, mag, K, "launch shapes")
+
+
+def _random_gemm_cases(n=10, seed=20261205):
+    """Seeded random grouped problems: skewed expert sizes (some empty, some several
+    tiles), K a multiple of 64 (so both the direct-to-LDS and the register-staged bodies
+    run) and Nout a multiple of 128 (so all three launch shapes run)."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        G = int(rng.integers(1, 65))
+        sizes = np.floor(rng.pareto(1.2, G) * 60).astype(np.int64)
+        sizes[rng.random(G) < 0.15] = 0
+        sizes = np.minimum(sizes, 1500)
+        K = int(rng.choice([64, 128, 192, 256, 384, 512, 1024]))
+        Nout = int(rng.choice([128, 256, 384, 512, 768]))
+        cases.append((tuple(int(v) for v in sizes), K, Nout))
+    return cases
+
+
+GEMM_RANDOM = _random_gemm_cases()
+
+
+@pytest.mark.parametrize("case", GEMM_RANDOM, ids=[f"G{len(c[0])}-rows{sum(c[0])}-K{c[1]}-N{c[2]}"
+                                                   for c in GEMM_RANDOM])
+def test_grouped_gemm_random(gpu_lib, case):
+    counts, K, Nout = case
+    G = len(counts)
+    rows = sum(counts)
+    say(f"grouped gemm random G={G} rows={rows} K={K} Nout={Nout}")
+    idx = np.concatenate([np.full(c, e, np.int32) for e, c in enumerate(counts)] +
+                         [np.zeros(0, np.int32)]).reshape(-1, 1)
+    rng = np.random.default_rng([G, rows, K, Nout])
+    idx = idx[rng.permutation(len(idx))]
+    ebkt = np.zeros(G, np.int32)
+    ref = oracle.dispatch_layout(idx, ebkt, 1, False)
+    lay = moedl.moe_dispatch_layout(dev(idx), dev(ebkt), 1, False)
+    tiles = _check_tiles(lay, ref, rows)
+    if rows == 0:
+        return
+    x = _bf16(rng, (rows, K))
+    w = _bf16(rng, (G, Nout, K), scale=0.1)
+    _check_gemm(x, w, ref, tiles, ctx=f"G={G} rows={rows} K={K} Nout={Nout}")
