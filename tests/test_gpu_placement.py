@@ -45,3 +45,35 @@ def test_placement_chain(gpu_lib):
     assert int(lay.bucket_offset[w.B].item()) == ref.R
     rr = oracle.dispatch_layout(w.topk_idx, wl.round_robin_buckets(w.G, w.B), w.B, True).R
     assert ref.R < rr
+
+
+def _random_cases(n=8, seed=20261206):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        G = int(rng.choice([2, 7, 64, 128, 256, 1000, 1024]))
+        k = int(rng.integers(1, min(16, G) + 1))
+        M = int(np.exp(rng.uniform(0, np.log(30000 // k))))
+        routing = "repeats" if rng.random() < 0.4 else "uniform"
+        divisors = [b for b in range(1, 65) if G % b == 0]  # equal-sized buckets
+        B = int(rng.choice(divisors))
+        cases.append((M, k, G, routing, B))
+    return cases
+
+
+PLACE_RANDOM = _random_cases()
+
+
+@pytest.mark.parametrize("case", PLACE_RANDOM, ids=[f"M{c[0]}-k{c[1]}-G{c[2]}-{c[3]}-B{c[4]}"
+                                                    for c in PLACE_RANDOM])
+def test_pair_counts_and_placement_random(gpu_lib, case):
+    """Seeded random routings: pair counts bit for bit, then the host greedy on the GPU
+    counts gives the oracle's map."""
+    M, k, G, routing, B = case
+    idx = wl.make_custom(M, 16, G, k, 1, routing=routing, seed=M + G).topk_idx
+    say(f"pair counts random M={M} k={k} G={G} {routing} B={B}")
+    C = moedl.moe_expert_pair_counts(dev(idx), G)
+    got = host(C)
+    want = oracle.pair_counts(idx, G)
+    assert np.array_equal(got, want)
+    assert np.array_equal(moedl.moe_place_experts(C, B), oracle.greedy_place(want, B))
