@@ -31,6 +31,15 @@ COMMON = [
     "-I", INCLUDE, "-I", CSRC,
 ]
 
+# Per-source additions.  layout.hip: no atomic optimizer.  It would turn the one-lane
+# fetch-add with which a layout tile leaves into a wave reduction that waits for the
+# returned value at once; the kernel issues that atomic early and reads the value only
+# at its end, so that the round trip overlaps the rest of the tile's work.  (Every other
+# atomic there on a wave-uniform address is on an error path.)
+EXTRA = {
+    "layout.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"],
+}
+
 LIBS = {
     "libmoedl.so": ["api.cpp", "layout.hip", "noalloc.hip", "dispatch.hip", "combine.hip",
                     "bucket.hip", "placement.hip", "gemm.hip"],
@@ -50,7 +59,8 @@ def _run(cmd: list[str]) -> None:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    _run([HIPCC, "-x", "hip", *COMMON, "-c", os.path.join(CSRC, src), "-o", obj])
+    _run([HIPCC, "-x", "hip", *COMMON, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src),
+          "-o", obj])
     return obj
 
 

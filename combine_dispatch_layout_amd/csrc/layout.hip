@@ -66,7 +66,10 @@ __device__ __forceinline__ int bits_for(int n) {  // bits needed for values in [
 // key[c] equals the caller's, among lanes with ok[c] set (meaningless where ok[c] is
 // false).  Lanes agree on a key when they agree on each of its nbits bits, one ballot
 // per bit.  The bit loop is outside the chunk loop and fully unrolled, so the ballots
-// of different chunks interleave instead of forming one long dependent chain.
+// of different chunks interleave instead of forming one long dependent chain.  Per bit
+// and chunk: m = the bit spread over the word, the ballot, and peers &= ~(ballot ^ m)
+// as one three-input logic op per half (v_bitop3; truth table 0x84 with the mask as
+// the middle operand, which reads the same whichever outer operand indexes first).
 template <int C, int MAXBITS>
 __device__ __forceinline__ void match_peers(const bool (&ok)[C], const int (&key)[C], int nbits,
                                             uint64_t (&peers)[C]) {
@@ -77,9 +80,12 @@ __device__ __forceinline__ void match_peers(const bool (&ok)[C], const int (&key
     if (bit < nbits) {  // uniform
 #pragma unroll
       for (int c = 0; c < C; ++c) {
-        const bool set = (key[c] >> bit) & 1;
-        const uint64_t bal = wave_ballot(set);
-        peers[c] &= set ? bal : ~bal;
+        const uint32_t m = (uint32_t)((int32_t)((uint32_t)key[c] << (31 - bit)) >> 31);
+        const uint64_t bal = wave_ballot(m != 0u);
+        const uint32_t lo = __builtin_amdgcn_bitop3_b32((uint32_t)bal, (uint32_t)peers[c], m, 0x84);
+        const uint32_t hi =
+            __builtin_amdgcn_bitop3_b32((uint32_t)(bal >> 32), (uint32_t)(peers[c] >> 32), m, 0x84);
+        peers[c] = ((uint64_t)hi << 32) | lo;
       }
     }
   }
@@ -172,24 +178,23 @@ __device__ __forceinline__ int64_t tile_end_entry(int32_t M, int32_t k, int tile
   return e < Mk ? e : Mk;
 }
 
-// Expert ranks of one tile of TT tokens (256 unless stated), NW waves of NC chunks
-// each (see wave_first_entry; NW * NC = (TT / 64) * KC covers the tile).  On return
-// (after a barrier): ec[c] / rc[c] hold the expert id (or kAbsent) and the rank inside
-// the tile of flat entry wave_first_entry<NC, TT>(tile, k, w) + c*64 + lane; totals[e] holds the tile's
-// count of expert e (totals may be global or LDS); lds.ids_s holds the tile's ids
-// (tile-local flat order) when keep_ids.
+// First half of tile_expert_ranks: ec[c] = the expert id of flat entry
+// wave_first_entry<NC, TT>(tile, k, w) + c*64 + lane, or kAbsent (past the end, or an
+// id outside [0, G), whose first flat index goes to lds.err_s), ok[c] = present;
+// lds.map_s holds the map and the per-wave counters are zero (both complete after the
+// barrier inside); lds.ids_s holds the tile's ids (tile-local flat order) when
+// keep_ids, written after that barrier: readers in other waves need another one.
 template <int KC, int NC, int NW = kTileWaves, int TT = kTileTokens>
-__device__ __forceinline__ void tile_expert_ranks(TileLds<KC, NW, TT>& lds, const int32_t* __restrict__ idx,
-                                                  int32_t M, int32_t k,
-                                                  const int32_t* __restrict__ ebkt, int32_t G,
-                                                  int32_t B, int tile, bool keep_ids,
-                                                  int32_t* totals, int (&ec)[NC], int (&rc)[NC]) {
+__device__ __forceinline__ void tile_load_ids(TileLds<KC, NW, TT>& lds, const int32_t* __restrict__ idx,
+                                              int32_t M, int32_t k,
+                                              const int32_t* __restrict__ ebkt, int32_t G,
+                                              int32_t B, int tile, bool keep_ids,
+                                              int (&ec)[NC], bool (&ok)[NC]) {
   static_assert(NC * NW <= KC * (TT / 64), "a wave's chunks must fit the tile's id store");
   constexpr int NT = NW * 64;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = wave_index();
-  const int nbits = bits_for(G);
   const int64_t wbase = wave_first_entry<NC, TT>(tile, k, w);
   const int64_t tend = tile_end_entry<TT>(M, k, tile);
   const int local0 = w * 64 * NC;  // tile-local index of the wave's first entry
@@ -212,7 +217,6 @@ __device__ __forceinline__ void tile_expert_ranks(TileLds<KC, NW, TT>& lds, cons
   __syncthreads();
 
   int my_err = kNoError;
-  bool ok[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     int e = ec[c];
@@ -224,10 +228,22 @@ __device__ __forceinline__ void tile_expert_ranks(TileLds<KC, NW, TT>& lds, cons
     ok[c] = e >= 0;
     ec[c] = e;
   }
-  uint64_t peers[NC];
-  match_peers<NC, kExpertBits>(ok, ec, nbits, peers);
-  stable_ranks<NC>(ok, ec, peers, lds.wcnt[w], rc);
   if (my_err != kNoError) atomicMin(&lds.err_s, my_err);
+}
+
+// Second half: the stable ranks of the loaded entries.  On return (after a barrier)
+// rc[c] is the rank inside the tile of entry c (meaningless where ec[c] is absent);
+// totals[e] (global or LDS, or null) holds the tile's count of expert e.
+template <int KC, int NC, int NW = kTileWaves, int TT = kTileTokens>
+__device__ __forceinline__ void tile_rank_entries(TileLds<KC, NW, TT>& lds, int32_t G,
+                                                  const bool (&ok)[NC], const int (&ec)[NC],
+                                                  int32_t* totals, int (&rc)[NC]) {
+  constexpr int NT = NW * 64;
+  const int tid = threadIdx.x;
+  const int w = wave_index();
+  uint64_t peers[NC];
+  match_peers<NC, kExpertBits>(ok, ec, bits_for(G), peers);
+  stable_ranks<NC>(ok, ec, peers, lds.wcnt[w], rc);
   __syncthreads();
 
   // cross-wave exclusive prefix per expert; the column total is the tile's count
@@ -239,7 +255,7 @@ __device__ __forceinline__ void tile_expert_ranks(TileLds<KC, NW, TT>& lds, cons
       lds.wcnt[ww][e] = run;
       run += v;
     }
-    totals[e] = run;
+    if (totals != nullptr) totals[e] = run;
   }
   __syncthreads();
 #pragma unroll
@@ -247,11 +263,28 @@ __device__ __forceinline__ void tile_expert_ranks(TileLds<KC, NW, TT>& lds, cons
     if (ec[c] >= 0) rc[c] += lds.wcnt[w][ec[c]];
 }
 
+// Expert ranks of one tile of TT tokens (256 unless stated), NW waves of NC chunks
+// each (see wave_first_entry; NW * NC = (TT / 64) * KC covers the tile).  On return
+// (after a barrier): ec[c] / rc[c] hold the expert id (or kAbsent) and the rank inside
+// the tile of flat entry wave_first_entry<NC, TT>(tile, k, w) + c*64 + lane; totals[e] holds the tile's
+// count of expert e (totals may be global or LDS); lds.ids_s holds the tile's ids
+// (tile-local flat order) when keep_ids.
+template <int KC, int NC, int NW = kTileWaves, int TT = kTileTokens>
+__device__ __forceinline__ void tile_expert_ranks(TileLds<KC, NW, TT>& lds, const int32_t* __restrict__ idx,
+                                                  int32_t M, int32_t k,
+                                                  const int32_t* __restrict__ ebkt, int32_t G,
+                                                  int32_t B, int tile, bool keep_ids,
+                                                  int32_t* totals, int (&ec)[NC], int (&rc)[NC]) {
+  bool ok[NC];
+  tile_load_ids<KC, NC, NW, TT>(lds, idx, M, k, ebkt, G, B, tile, keep_ids, ec, ok);
+  tile_rank_entries<KC, NC, NW, TT>(lds, G, ok, ec, totals, rc);
+}
+
 // Dedup ranks of one tile (token view: token w*64 + lane of the tile in waves w <
 // TT / 64; later waves hold no token).  Needs lds.ids_s from tile_expert_ranks.
 // On return (after a barrier): eb[j] is the bucket of the lane's token's j-th entry or
 // kBadBucket, dl[j] the token's rank among the tile's tokens that send to that
-// bucket; btotals[b] the tile's distinct-token count of bucket b.
+// bucket; btotals[b] (unless null) the tile's distinct-token count of bucket b.
 template <int KC, int NW = kTileWaves, int TT = kTileTokens>
 __device__ __forceinline__ void tile_dedup_ranks(TileLds<KC, NW, TT>& lds, int32_t M, int32_t k, int32_t B, int tile,
                                  int32_t* btotals, int (&eb)[KC], int (&dl)[KC]) {
@@ -296,7 +329,7 @@ __device__ __forceinline__ void tile_dedup_ranks(TileLds<KC, NW, TT>& lds, int32
       lds.wbcnt[ww][tid] = run;
       run += v;
     }
-    btotals[tid] = run;
+    if (btotals != nullptr) btotals[tid] = run;
   }
   __syncthreads();
   const int wt = token_wave ? w : 0;  // waves without tokens read a valid row, unused
@@ -306,6 +339,32 @@ __device__ __forceinline__ void tile_dedup_ranks(TileLds<KC, NW, TT>& lds, int32
     const int base = lds.wbcnt[wt][b];
     const uint64_t bal = lds.wbal[wt][b];
     dl[j] = eb[j] != kBadBucket ? base + __builtin_popcountll(bal & below) : -1;
+  }
+}
+
+// Distinct-token counts of the tile's buckets, token view as in tile_dedup_ranks:
+// bcnt[b] gains one for every token of the tile that sends to bucket b (LDS adds, no
+// ranks).  bcnt must be zero and lds.ids_s / lds.map_s complete; callers put a barrier
+// after it.
+template <int KC, int NW, int TT>
+__device__ __forceinline__ void tile_bucket_counts(TileLds<KC, NW, TT>& lds, int32_t M, int32_t k,
+                                                   int tile, int32_t* bcnt) {
+  const int lane = threadIdx.x & 63;
+  const int w = wave_index();
+  const int64_t t = (int64_t)tile * TT + (int64_t)w * 64 + lane;
+  if (w >= TT / 64 || t >= M) return;
+  const int* my_ids = lds.ids_s + (w * 64 + lane) * k;
+  int ev[KC], m[KC];
+#pragma unroll
+  for (int j = 0; j < KC; ++j) ev[j] = j < k ? my_ids[j] : kAbsent;
+#pragma unroll
+  for (int j = 0; j < KC; ++j) m[j] = lds.map_s[ev[j] >= 0 ? ev[j] : 0];
+  uint64_t seen = 0;
+#pragma unroll
+  for (int j = 0; j < KC; ++j) {
+    if (ev[j] < 0 || m[j] == kBadBucket || ((seen >> m[j]) & 1ull)) continue;
+    seen |= 1ull << m[j];
+    atomicAdd(bcnt + m[j], 1);
   }
 }
 
@@ -335,16 +394,68 @@ struct OrderLds {
   int32_t wave_sums[NT / 64];
 };
 
+template <int NT>
+constexpr int order_chunks() { return (kMaxE + NT - 1) / NT; }  // 64-expert chunks per wave
+
+// Positions of the experts in (bucket, id) order, from the map alone.  NT-thread
+// workgroup; wave w ranks a contiguous range of experts (w * per + c * 64 + lane) so
+// the cross-wave prefix keeps id order.  On return (after a barrier) pos[c] is the
+// position of expert w * per + c * 64 + lane (-1 past G) and lds.base[b] the first
+// position of bucket b.  A bad map entry is ranked as bucket B - 1 (callers report
+// it).
+template <int NT>
+__device__ void expert_sigma_positions(OrderLds<NT>& lds, const unsigned char* map_s,
+                                       int32_t G, int32_t B, int (&pos)[order_chunks<NT>()]) {
+  constexpr int NW = NT / 64;
+  constexpr int CH = order_chunks<NT>();
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = wave_index();
+  const int per = ((G + NW - 1) / NW + 63) / 64 * 64;  // experts per wave, whole chunks
+  for (int i = tid; i < NW * kMaxB; i += NT) lds.wbc[i / kMaxB][i % kMaxB] = 0;
+  __syncthreads();
+
+  const int nbits = bits_for(B);
+  int rk[CH];
+  int bk[CH];
+  bool okc[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int e = w * per + c * 64 + lane;
+    okc[c] = c * 64 < per && e < G;
+    int b = okc[c] ? (int)map_s[e] : 0;
+    bk[c] = b < B ? b : B - 1;  // a bad map entry is reported by status; keep it in range
+  }
+  uint64_t peers[CH];
+  match_peers<CH, kBucketBits>(okc, bk, nbits, peers);
+  stable_ranks<CH>(okc, bk, peers, lds.wbc[w], rk);
+  __syncthreads();
+  if (tid < B) {
+    int run = 0;
+    for (int q = 0; q < NW; ++q) {
+      const int v = lds.wbc[q][tid];
+      lds.wbc[q][tid] = run;
+      run += v;
+    }
+    lds.base[tid] = run;
+  }
+  __syncthreads();
+  small_exclusive_scan(lds.base, lds.base, B, false);
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < CH; ++c)
+    pos[c] = okc[c] ? lds.base[bk[c]] + lds.wbc[w][bk[c]] + rk[c] : -1;
+}
+
 // Offsets of expert runs laid out in (bucket, id) order, from per-expert counts
-// cnt[G] (LDS).  NT-thread workgroup; wave w handles a contiguous range of experts so
-// the cross-wave prefix keeps id order.  A map whose bucket never decreases with the
+// cnt[G] (LDS).  NT-thread workgroup.  A map whose bucket never decreases with the
 // id takes a fast path (id order).  Writes offset[e] (global or LDS).
 template <int NT>
 __device__ void expert_order_offsets(OrderLds<NT>& lds, const unsigned char* map_s,
                                      const int32_t* cnt, int32_t G, int32_t B,
                                      int32_t* offset) {
   constexpr int NW = NT / 64;
-  constexpr int CH = (kMaxE + NT - 1) / NT;  // chunks of 64 experts per wave, at most
+  constexpr int CH = order_chunks<NT>();
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = wave_index();
@@ -376,45 +487,12 @@ __device__ void expert_order_offsets(OrderLds<NT>& lds, const unsigned char* map
     return;
   }
 
-  for (int i = tid; i < NW * kMaxB; i += NT) lds.wbc[i / kMaxB][i % kMaxB] = 0;
-  __syncthreads();
-
-  const int nbits = bits_for(B);
-  int rk[CH];
-  int bk[CH];
-  bool okc[CH];
-#pragma unroll
-  for (int c = 0; c < CH; ++c) {
-    const int e = w * per + c * 64 + lane;
-    okc[c] = c * 64 < per && e < G;
-    int b = okc[c] ? (int)map_s[e] : 0;
-    bk[c] = b < B ? b : B - 1;  // a bad map entry is reported by status; keep it in range
-  }
-  uint64_t peers[CH];
-  match_peers<CH, kBucketBits>(okc, bk, nbits, peers);
-  stable_ranks<CH>(okc, bk, peers, lds.wbc[w], rk);
-  __syncthreads();
-  if (tid < B) {
-    int run = 0;
-    for (int q = 0; q < NW; ++q) {
-      const int v = lds.wbc[q][tid];
-      lds.wbc[q][tid] = run;
-      run += v;
-    }
-    lds.base[tid] = run;
-  }
-  __syncthreads();
-  small_exclusive_scan(lds.base, lds.base, B, false);
-  __syncthreads();
   int pos[CH];
+  expert_sigma_positions<NT>(lds, map_s, G, B, pos);
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     const int e = w * per + c * 64 + lane;
-    pos[c] = -1;
-    if (c * 64 < per && e < G) {
-      pos[c] = lds.base[bk[c]] + lds.wbc[w][bk[c]] + rk[c];
-      lds.arr[pos[c]] = cnt[e];
-    }
+    if (pos[c] >= 0) lds.arr[pos[c]] = cnt[e];
   }
   __syncthreads();
   // exclusive scan of arr[0, G): thread tid owns CH consecutive entries
@@ -942,19 +1020,18 @@ __device__ __forceinline__ bool all_published(u32x4 v) {
   return v[0] != 0u && v[1] != 0u && v[2] != 0u && v[3] != 0u;
 }
 
-// pre[c] = sum over rows t < tile and tot[c] = sum over all T rows of the Cp columns
-// (Cp % 4 == 0) of the row-major rows[T][Cp] (values stored + 1), into LDS, by an
-// NT-thread workgroup whose threads [T0, NT) read: 16-byte quads with agent-scope
-// buffer loads, PB at a time, reloading those not yet fully published.  (Threads
-// below T0 have stores in flight; a wave's loads complete only after its earlier
-// stores, so they take no part in the reads.)  When a row has fewer quads than there
-// are reading threads, `stride` groups of them take interleaved rows and seg_* (4 *
-// NT ints each) join the groups.  Returns false if some quad was still unpublished
-// when the poll gave up.
+// pre[c] += sum over rows t < tile and tot[c] += sum over all T rows of the Cp
+// columns (Cp % 4 == 0) of the row-major rows[T][Cp] (values stored + 1), into LDS
+// (zero on entry), by an NT-thread workgroup whose threads [T0, NT) read: 16-byte
+// quads with agent-scope buffer loads, PB at a time, reloading those not yet fully
+// published.  (Threads below T0 have stores in flight; a wave's loads complete only
+// after its earlier stores, so they take no part in the reads.)  When a row has fewer
+// quads than there are reading threads, `stride` groups of them take interleaved
+// rows; every reader adds its partial sums with LDS adds.  Ends after a barrier;
+// returns false if some quad was still unpublished when the poll gave up.
 template <int NT, int PB, int T0>
 __device__ __forceinline__ bool poll_column_sums(const int32_t* rows, int T, int Cp, int tile,
-                                                 int32_t* pre, int32_t* tot, int32_t* seg_pre,
-                                                 int32_t* seg_tot) {
+                                                 int32_t* pre, int32_t* tot) {
   constexpr int NP = NT - T0;  // reading threads
   const int tid = threadIdx.x - T0;
   const int Q = Cp / 4;
@@ -997,28 +1074,14 @@ __device__ __forceinline__ bool poll_column_sums(const int32_t* rows, int T, int
       done = done && pend == 0u;
     }
     if (active) {
-      int32_t* dp = wide ? pre + 4 * q : seg_pre + g * Cp + 4 * q;
-      int32_t* dt = wide ? tot + 4 * q : seg_tot + g * Cp + 4 * q;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        dp[i] = (int)p[i];
-        dt[i] = (int)a[i];
+        atomicAdd(pre + 4 * q + i, (int)p[i]);
+        atomicAdd(tot + 4 * q + i, (int)a[i]);
       }
     }
   }
   __syncthreads();
-  if (!wide) {
-    for (int c = threadIdx.x; c < Cp; c += NT) {
-      int pp = 0, ss = 0;
-      for (int g = 0; g < stride; ++g) {
-        pp += seg_pre[g * Cp + c];
-        ss += seg_tot[g * Cp + c];
-      }
-      pre[c] = pp;
-      tot[c] = ss;
-    }
-    __syncthreads();
-  }
   return done;
 }
 
@@ -1042,18 +1105,18 @@ __global__ __launch_bounds__((onepass_waves<KC, TT>() * 64)) void layout_onepass
   constexpr int NT = NW * 64;
   constexpr int NC = (TT / 64) * KC / NW;  // chunks per wave
   static_assert(NC >= 1 && NC * NW == (TT / 64) * KC, "the waves cover the tile");
-  static_assert(8 * NT <= NW * kMaxE, "column-sum scratch fits the spent rank counters");
   __shared__ TileLds<KC, NW, TT> lds;
   __shared__ OrderLds<NT> olds;
   // a tile's row: expert counts [0, G), bucket counts [Gp, Gp + B) (dedup), zero pads
   __shared__ int32_t pre_s[kRegionCols];
   __shared__ int32_t tot_s[kRegionCols];
   __shared__ int32_t off_s[kMaxE];
-  __shared__ int32_t bsum_s[kMaxB];
+  __shared__ int32_t inv_s[kMaxE];       // the expert at each (bucket, id) position
+  __shared__ int32_t scan_s[kMaxE + 1];  // exclusive scan of the counts in that order
+  __shared__ int32_t base_s[kMaxB + 1];  // first position of each bucket
   __shared__ int32_t boff_s[kMaxB + 1];
   __shared__ int32_t err_s;
   __shared__ int32_t mapbad_s;
-  __shared__ int32_t expired_s;
   __shared__ int32_t sorted_map_s;
 
   const int T = (int)gridDim.x;
@@ -1064,40 +1127,51 @@ __global__ __launch_bounds__((onepass_waves<KC, TT>() * 64)) void layout_onepass
   const int64_t Mk = (int64_t)M * k;
   const int Gp = (G + 3) & ~3;
   const int Cp = dedup ? Gp + ((B + 3) & ~3) : Gp;  // row pitch of this call, in ints
-  // which region this call publishes in, and what the previous call left in the other
-  const uint32_t parity = __hip_atomic_load(header + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 1u;
-  const int prev_T = (int)__hip_atomic_load(header + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const int prev_Cp = (int)__hip_atomic_load(header + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // which region this call publishes in, and what the previous call left in the other.
+  // Plain loads: these words were last written by an earlier launch (visible to this
+  // one like any kernel's output to the next), and this launch rewrites them only
+  // after every tile has published, i.e. after every tile has read them.  (Device-
+  // coherent loads would take the slow path, and the in-order completion of vector
+  // memory operations would make the topk_idx loads behind them wait as long.)
+  const uint32_t parity = header[1] & 1u;
+  const int prev_T = (int)header[2];
+  const int prev_Cp = (int)header[3];
   int32_t* const rows = parity ? region1 : region0;
   int32_t* const old_rows = parity ? region0 : region1;
-  if (tid < kMaxB) bsum_s[tid] = 0;
   if (tid == 0) {
     err_s = kNoError;
     mapbad_s = kNoError;
-    expired_s = 0;
   }
-  for (int c = G + tid; c < Cp; c += NT) pre_s[c] = 0;  // pads (buckets below)
+  for (int c = tid; c < Cp; c += NT) pre_s[c] = 0;
 
-  // this tile's ranks; its row (in pre_s until the column sums) goes to the region
-  int ec[NC], rc[NC];
-  tile_expert_ranks<KC, NC, NW, TT>(lds, idx, M, k, ebkt, G, B, tile, dedup != 0, pre_s, ec, rc);
+  // The counts go out first: per-tile histograms are cheap (LDS adds), while the
+  // stable ranks (ballot matching) are the tile's longest compute.  So the ranks, and
+  // the (bucket, id) order of the experts, run while the other tiles' counts travel.
+  int ec[NC];
+  bool ok[NC];
+  tile_load_ids<KC, NC, NW, TT>(lds, idx, M, k, ebkt, G, B, tile, dedup != 0, ec, ok);
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+    if (ok[c]) atomicAdd(pre_s + ec[c], 1);
   if (w == NW - 1) {  // is the map in range and nondecreasing in the expert id?
-    bool ok = true;
+    bool good = true;
 #pragma unroll 4
     for (int e = lane; e < G; e += 64) {
       const int m = lds.map_s[e];
       const int m1 = lds.map_s[e + 1 < G ? e + 1 : e];
-      ok &= (m != kBadBucket) & (m <= m1);
+      good &= (m != kBadBucket) & (m <= m1);
     }
-    const bool sorted = wave_ballot(!ok) == 0;
+    const bool sorted = wave_ballot(!good) == 0;
     if (lane == 0) sorted_map_s = sorted;  // read after the barriers below
   }
-  int eb[KC], dl[KC];
-  if (dedup) tile_dedup_ranks<KC, NW, TT>(lds, M, k, B, tile, pre_s + Gp, eb, dl);
+  if (dedup) {
+    __syncthreads();  // lds.ids_s complete
+    tile_bucket_counts<KC, NW, TT>(lds, M, k, tile, pre_s + Gp);
+  }
+  __syncthreads();
 
   // Wave 0 publishes (value + 1; nobody waits for these stores, readers poll the
-  // words) and then clears this tile's share of the previous call's rows; the other
-  // waves read.
+  // words) and then clears this tile's share of the previous call's rows.
   if (w == 0) {
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(rows + (int64_t)tile * Cp), (short)0, Cp * 4, kRawBufferWord3);
@@ -1119,10 +1193,43 @@ __global__ __launch_bounds__((onepass_waves<KC, TT>() * 64)) void layout_onepass
       __hip_atomic_store(old_rows + kRegionErrOffset + lane, 0, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
   }
-  __syncthreads();  // pre_s and the rank counters are overwritten below
 
-  // column sums over all tiles' rows: this tile's prefix and the totals (scratch: the
-  // per-wave rank counters, no longer needed).  The error words are polled too.
+  // While the counts travel (a store and a load across the chip take longer than
+  // the work below): this tile's ranks (the first barrier inside also orders the
+  // publication's reads of pre_s before it is overwritten below) ...
+  int rc[NC];
+  tile_rank_entries<KC, NC, NW, TT>(lds, G, ok, ec, nullptr, rc);
+  int eb[KC], dl[KC];
+  if (dedup) tile_dedup_ranks<KC, NW, TT>(lds, M, k, B, tile, nullptr, eb, dl);
+  // ... and the experts' (bucket, id) order: id order for a contiguous map, where the
+  // buckets (map[e-1], map[e]] start at expert e; else ranked by bucket
+  if (sorted_map_s) {
+    for (int e = tid; e < G; e += NT) {
+      const int b1 = lds.map_s[e];
+      for (int b = e == 0 ? 0 : lds.map_s[e - 1] + 1; b <= b1; ++b) base_s[b] = e;
+      if (e == G - 1)
+        for (int b = b1 + 1; b <= B; ++b) base_s[b] = G;
+    }
+  } else {
+    for (int e = tid; e < G; e += NT)
+      if (lds.map_s[e] == kBadBucket) atomicMin(&mapbad_s, e);
+    constexpr int CH = order_chunks<NT>();
+    const int per = ((G + NW - 1) / NW + 63) / 64 * 64;
+    int pos[CH];
+    expert_sigma_positions<NT>(olds, lds.map_s, G, B, pos);
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+      if (pos[c] >= 0) inv_s[pos[c]] = w * per + c * 64 + lane;
+    if (tid <= B) base_s[tid] = tid < B ? olds.base[tid] : G;
+  }
+  for (int c = tid; c < Cp; c += NT) {  // the published row is no longer read
+    pre_s[c] = 0;
+    tot_s[c] = 0;
+  }
+  __syncthreads();
+
+  // column sums over all tiles' rows: this tile's prefix and the totals.  The error
+  // words are polled too.
   bool done = true;
   if (w == 1 && lane < T) {
     uint32_t e = 0;
@@ -1136,51 +1243,60 @@ __global__ __launch_bounds__((onepass_waves<KC, TT>() * 64)) void layout_onepass
     if (done && (int)(e - 1u) != kNoError) atomicMin(&err_s, (int)(e - 1u));
   }
   constexpr int PB = (KC >= 16 || TT > kTileTokens) ? 4 : 8;  // quads polled at once (registers)
-  done = poll_column_sums<NT, PB, 64>(rows, T, Cp, tile, pre_s, tot_s, &lds.wcnt[0][0],
-                                      &lds.wcnt[0][0] + 4 * NT) && done;
-  if (!done) expired_s = 1;  // read after the barriers below
+  done = poll_column_sums<NT, PB, 64>(rows, T, Cp, tile, pre_s, tot_s) && done;
+  const bool expired = __syncthreads_or(!done);
   const int32_t* bpre_s = pre_s + Gp;  // dedup: this tile's prefix of each bucket
 
-  // expert offsets in (bucket, id) order and bucket offsets (dedup: the bucket totals
-  // are columns Gp.. of the sums)
-  if (sorted_map_s) {
-    // (bucket, id) order is id order: wave 0 scans the counts (lane i holds a run of
-    // `per` consecutive experts); with dedup off each bucket starts at its first
-    // expert, so the bucket offsets fall out of the same scan.  With dedup, wave 1
-    // scans the distinct-token counts of the buckets.
-    if (w == 0) {
-      const int per = (G + 63) / 64;
+  // leave: this tile's reads of the region are complete.  The count of tiles whose
+  // poll expired rides in the high half.  The returned count is looked at only at the
+  // end, so the round trip overlaps the offsets and the slots (the library builds this
+  // file without the atomic optimizer, which would wait for it here).
+  const uint32_t mine = 1u + (expired ? 0x10000u : 0u);
+  uint32_t before = 0;
+  if (tid == 0)
+    before = __hip_atomic_fetch_add(header, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  // expert offsets: wave 0 scans the totals in (bucket, id) order, 8 positions per
+  // lane and round (all LDS reads of a round in flight together); bucket offsets are
+  // the scan at each bucket's first position (dedup: wave 1 scans the bucket totals,
+  // columns Gp.. of the sums)
+  if (w == 0) {
+    constexpr int kPer = 8;
+    const bool sorted = sorted_map_s;
+    int carry = 0;
+    for (int r0 = 0; r0 < G; r0 += 64 * kPer) {
+      int ex[kPer], v[kPer];
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const int i = r0 + lane * kPer + u;
+        const int ic = i < G ? i : G - 1;
+        ex[u] = sorted ? ic : inv_s[ic];
+      }
       int sum = 0;
-      for (int u = 0; u < per; ++u) {
-        const int e = lane * per + u;
-        sum += e < G ? tot_s[e] : 0;
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        v[u] = r0 + lane * kPer + u < G ? tot_s[ex[u]] : 0;
+        sum += v[u];
       }
-      int run = wave_inclusive_sum(sum) - sum;
-      for (int u = 0; u < per; ++u) {
-        const int e = lane * per + u;
-        if (e < G) {
-          off_s[e] = run;
-          if (!dedup) {  // buckets (map[e-1], map[e]] begin here; past the last, the end
-            const int b1 = lds.map_s[e];
-            for (int b = e == 0 ? 0 : lds.map_s[e - 1] + 1; b <= b1; ++b) boff_s[b] = run;
-            if (e == G - 1)
-              for (int b = b1 + 1; b <= B; ++b) boff_s[b] = run + tot_s[e];
-          }
-          run += tot_s[e];
+      const int incl = wave_inclusive_sum(sum);
+      int run = carry + incl - sum;
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const int i = r0 + lane * kPer + u;
+        if (i < G) {
+          off_s[ex[u]] = run;
+          scan_s[i] = run;
         }
+        run += v[u];
       }
+      carry += __builtin_amdgcn_readlane(incl, 63);
     }
-    if (dedup) small_exclusive_scan(tot_s + Gp, boff_s, B, true, 1);
-    __syncthreads();
-  } else {
-    for (int e = tid; e < G; e += NT) {
-      if (lds.map_s[e] == kBadBucket) atomicMin(&mapbad_s, e);
-      else atomicAdd(&bsum_s[lds.map_s[e]], tot_s[e]);
-    }
-    expert_order_offsets<NT>(olds, lds.map_s, tot_s, G, B, off_s);
-    small_exclusive_scan(dedup ? tot_s + Gp : bsum_s, boff_s, B, true);
-    __syncthreads();
+    if (lane == 0) scan_s[G] = carry;
   }
+  if (dedup) small_exclusive_scan(tot_s + Gp, boff_s, B, true, 1);
+  __syncthreads();
+  if (!dedup && tid <= B) boff_s[tid] = scan_s[base_s[tid]];
+  __syncthreads();
 
   if (tile == 0) {
     for (int e = tid; e < G; e += NT) {
@@ -1205,36 +1321,41 @@ __global__ __launch_bounds__((onepass_waves<KC, TT>() * 64)) void layout_onepass
       }
     }
   }
-  if (dedup && w < TT / 64) {
-    const int64_t t = (int64_t)tile * TT + (int64_t)w * 64 + lane;
-    const int64_t cap = (int64_t)M * (k < B ? k : B);
-    if (t < M) {
+  if (dedup) {
+    // send rows are found in the token view; they go through LDS (the tile's id store,
+    // no longer read) so that they are stored in flat order, like the slots
+    if (w < TT / 64) {
+      const int64_t t = (int64_t)tile * TT + (int64_t)w * 64 + lane;
+      const int64_t cap = (int64_t)M * (k < B ? k : B);
+      if (t < M) {
 #pragma unroll
-      for (int j = 0; j < KC; ++j) {
-        if (j < k) {
-          const int r = eb[j] != kBadBucket ? boff_s[eb[j]] + bpre_s[eb[j]] + dl[j] : -1;
-          send_row[t * k + j] = r;
-          if (r >= 0 && r < cap) send_token[r] = (int)t;
+        for (int j = 0; j < KC; ++j) {
+          if (j < k) {
+            const int r = eb[j] != kBadBucket ? boff_s[eb[j]] + bpre_s[eb[j]] + dl[j] : -1;
+            lds.ids_s[(w * 64 + lane) * k + j] = r;
+            if (r >= 0 && r < cap) send_token[r] = (int)t;
+          }
         }
       }
     }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int64_t f = wbase + (int64_t)c * 64 + lane;
+      if (f < tend) send_row[f] = lds.ids_s[w * 64 * NC + c * 64 + lane];
+    }
   }
 
-  // leave: this tile's reads of the region are complete (consumed before the barriers
-  // above).  The count of tiles whose poll expired rides in the high half.
-  if (tid == 0) {
-    const uint32_t mine = 1u + (expired_s ? 0x10000u : 0u);
-    const uint32_t now =
-        __hip_atomic_fetch_add(header, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + mine;
-    if ((now & 0xFFFFu) == (uint32_t)T) {
-      status[0] = (now >> 16) ? MOE_LAYOUT_STATUS_WAIT_EXPIRED
-                  : mapbad_s != kNoError ? -(mapbad_s + 1)
-                  : (err_s != kNoError ? err_s + 1 : 0);
-      __hip_atomic_store(header + 1, parity ^ 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(header + 2, (uint32_t)T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(header + 3, (uint32_t)Cp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(header, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+  // the last tile to leave writes the status and hands the region to the next call
+  const uint32_t now = before + mine;
+  if (tid == 0 && (now & 0xFFFFu) == (uint32_t)T) {
+    status[0] = (now >> 16) ? MOE_LAYOUT_STATUS_WAIT_EXPIRED
+                : mapbad_s != kNoError ? -(mapbad_s + 1)
+                : (err_s != kNoError ? err_s + 1 : 0);
+    __hip_atomic_store(header + 1, parity ^ 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(header + 2, (uint32_t)T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(header + 3, (uint32_t)Cp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(header, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
