@@ -1023,8 +1023,11 @@ __device__ __forceinline__ bool all_published(u32x4 v) {
 // pre[c] += sum over rows t < tile and tot[c] += sum over all T rows of the Cp
 // columns (Cp % 4 == 0) of the row-major rows[T][Cp] (values stored + 1), into LDS
 // (zero on entry), by an NT-thread workgroup whose threads [T0, NT) read: 16-byte
-// quads with agent-scope buffer loads, PB at a time, reloading those not yet fully
-// published.  (Threads below T0 have stores in flight; a wave's loads complete only
+// quads, PB at a time, reloading those not yet fully published.  The first attempt
+// uses plain loads: in one launch a word of the region is either still zero (cleared
+// by the previous call, and no stale line survives the launch boundary) or holds its
+// final value, so a cached copy can only show a quad as unpublished, never a wrong
+// count.  Reloads use agent-scope loads, which do not hit a stale cached line.  (Threads below T0 have stores in flight; a wave's loads complete only
 // after its earlier stores, so they take no part in the reads.)  When a row has fewer
 // quads than there are reading threads, `stride` groups of them take interleaved
 // rows; every reader adds its partial sums with LDS adds.  Ends after a barrier;
@@ -1052,13 +1055,24 @@ __device__ __forceinline__ bool poll_column_sums(const int32_t* rows, int T, int
       for (int i = 0; i < PB; ++i) pend |= (u0 + i < n ? 1u : 0u) << i;
       for (int spin = 0; pend != 0u && spin < kSpinLimit; ++spin) {
         u32x4 v[PB];
+        if (spin == 0) {
 #pragma unroll
-        for (int i = 0; i < PB; ++i) {
-          v[i] = u32x4{0, 0, 0, 0};
-          if ((pend >> i) & 1u)
-            v[i] = __builtin_bit_cast(
-                u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                           rs, ((g + (u0 + i) * stride) * Cp + 4 * q) * 4, 0, kSc1));
+          for (int i = 0; i < PB; ++i) {
+            v[i] = u32x4{0, 0, 0, 0};
+            if ((pend >> i) & 1u)
+              v[i] = __builtin_bit_cast(
+                  u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                             rs, ((g + (u0 + i) * stride) * Cp + 4 * q) * 4, 0, 0));
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < PB; ++i) {
+            v[i] = u32x4{0, 0, 0, 0};
+            if ((pend >> i) & 1u)
+              v[i] = __builtin_bit_cast(
+                  u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                             rs, ((g + (u0 + i) * stride) * Cp + 4 * q) * 4, 0, kSc1));
+          }
         }
 #pragma unroll
         for (int i = 0; i < PB; ++i) {
