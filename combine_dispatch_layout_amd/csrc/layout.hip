@@ -1167,17 +1167,6 @@ __global__ __launch_bounds__((onepass_waves<KC, TT>() * 64)) void layout_onepass
 #pragma unroll
   for (int c = 0; c < NC; ++c)
     if (ok[c]) atomicAdd(pre_s + ec[c], 1);
-  if (w == NW - 1) {  // is the map in range and nondecreasing in the expert id?
-    bool good = true;
-#pragma unroll 4
-    for (int e = lane; e < G; e += 64) {
-      const int m = lds.map_s[e];
-      const int m1 = lds.map_s[e + 1 < G ? e + 1 : e];
-      good &= (m != kBadBucket) & (m <= m1);
-    }
-    const bool sorted = wave_ballot(!good) == 0;
-    if (lane == 0) sorted_map_s = sorted;  // read after the barriers below
-  }
   if (dedup) {
     __syncthreads();  // lds.ids_s complete
     tile_bucket_counts<KC, NW, TT>(lds, M, k, tile, pre_s + Gp);
@@ -1206,6 +1195,17 @@ __global__ __launch_bounds__((onepass_waves<KC, TT>() * 64)) void layout_onepass
     if (tile == 0 && lane < prev_T)
       __hip_atomic_store(old_rows + kRegionErrOffset + lane, 0, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (w == NW - 1) {  // is the map in range and nondecreasing in the expert id?
+    bool good = true;
+#pragma unroll 4
+    for (int e = lane; e < G; e += 64) {
+      const int m = lds.map_s[e];
+      const int m1 = lds.map_s[e + 1 < G ? e + 1 : e];
+      good &= (m != kBadBucket) & (m <= m1);
+    }
+    const bool sorted = wave_ballot(!good) == 0;
+    if (lane == 0) sorted_map_s = sorted;  // read after the barriers below
   }
 
   // While the counts travel (a store and a load across the chip take longer than
