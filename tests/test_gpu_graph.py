@@ -42,7 +42,7 @@ def _replay_and_compare(fn, outputs, ctx):
             assert torch.equal(o, w_), f"{ctx}: replay {r}, output {i} differs"
 
 
-@pytest.mark.parametrize("cfg,M", [(1, None), (3, 1000)])
+@pytest.mark.parametrize("cfg,M", [(1, None), (3, 1000), (3, None)])
 @pytest.mark.parametrize("dedup", [False, True])
 def test_pipeline_in_graph(gpu_lib, cfg, M, dedup):
     w = wl.make_workload(cfg, M=M)
