@@ -231,23 +231,24 @@ __device__ __forceinline__ void tile_load_ids(TileLds<KC, NW, TT>& lds, const in
   if (my_err != kNoError) atomicMin(&lds.err_s, my_err);
 }
 
-// Second half: the stable ranks of the loaded entries.  On return (after a barrier)
-// rc[c] is the rank inside the tile of entry c (meaningless where ec[c] is absent);
-// totals[e] (global or LDS, or null) holds the tile's count of expert e.
-template <int KC, int NC, int NW = kTileWaves, int TT = kTileTokens>
-__device__ __forceinline__ void tile_rank_entries(TileLds<KC, NW, TT>& lds, int32_t G,
-                                                  const bool (&ok)[NC], const int (&ec)[NC],
-                                                  int32_t* totals, int (&rc)[NC]) {
-  constexpr int NT = NW * 64;
-  const int tid = threadIdx.x;
-  const int w = wave_index();
+// Second half: the stable ranks of the loaded entries, in three phases that callers
+// separate with barriers (tile_rank_entries below; the one-launch layout interleaves
+// them with the dedup ranks' phases).  After the last, rc[c] is the rank inside the
+// tile of entry c (meaningless where ec[c] is absent); totals[e] (global or LDS, or
+// null) holds the tile's count of expert e after the second.
+template <int KC, int NC, int NW, int TT>
+__device__ __forceinline__ void rank_phase_match(TileLds<KC, NW, TT>& lds, int32_t G,
+                                                 const bool (&ok)[NC], const int (&ec)[NC],
+                                                 int (&rc)[NC]) {
   uint64_t peers[NC];
   match_peers<NC, kExpertBits>(ok, ec, bits_for(G), peers);
-  stable_ranks<NC>(ok, ec, peers, lds.wcnt[w], rc);
-  __syncthreads();
-
+  stable_ranks<NC>(ok, ec, peers, lds.wcnt[wave_index()], rc);
+}
+template <int KC, int NW, int TT>
+__device__ __forceinline__ void rank_phase_prefix(TileLds<KC, NW, TT>& lds, int32_t G,
+                                                  int32_t* totals) {
   // cross-wave exclusive prefix per expert; the column total is the tile's count
-  for (int e = tid; e < G; e += NT) {
+  for (int e = threadIdx.x; e < G; e += NW * 64) {
     int run = 0;
 #pragma unroll
     for (int ww = 0; ww < NW; ++ww) {
@@ -257,10 +258,25 @@ __device__ __forceinline__ void tile_rank_entries(TileLds<KC, NW, TT>& lds, int3
     }
     if (totals != nullptr) totals[e] = run;
   }
-  __syncthreads();
+}
+template <int KC, int NC, int NW, int TT>
+__device__ __forceinline__ void rank_phase_finish(TileLds<KC, NW, TT>& lds, const int (&ec)[NC],
+                                                  int (&rc)[NC]) {
+  const int w = wave_index();
 #pragma unroll
   for (int c = 0; c < NC; ++c)
     if (ec[c] >= 0) rc[c] += lds.wcnt[w][ec[c]];
+}
+
+template <int KC, int NC, int NW = kTileWaves, int TT = kTileTokens>
+__device__ __forceinline__ void tile_rank_entries(TileLds<KC, NW, TT>& lds, int32_t G,
+                                                  const bool (&ok)[NC], const int (&ec)[NC],
+                                                  int32_t* totals, int (&rc)[NC]) {
+  rank_phase_match<KC, NC, NW, TT>(lds, G, ok, ec, rc);
+  __syncthreads();
+  rank_phase_prefix<KC, NW, TT>(lds, G, totals);
+  __syncthreads();
+  rank_phase_finish<KC, NC, NW, TT>(lds, ec, rc);
 }
 
 // Expert ranks of one tile of TT tokens (256 unless stated), NW waves of NC chunks
@@ -282,19 +298,19 @@ __device__ __forceinline__ void tile_expert_ranks(TileLds<KC, NW, TT>& lds, cons
 
 // Dedup ranks of one tile (token view: token w*64 + lane of the tile in waves w <
 // TT / 64; later waves hold no token).  Needs lds.ids_s from tile_expert_ranks.
-// On return (after a barrier): eb[j] is the bucket of the lane's token's j-th entry or
-// kBadBucket, dl[j] the token's rank among the tile's tokens that send to that
-// bucket; btotals[b] (unless null) the tile's distinct-token count of bucket b.
-template <int KC, int NW = kTileWaves, int TT = kTileTokens>
-__device__ __forceinline__ void tile_dedup_ranks(TileLds<KC, NW, TT>& lds, int32_t M, int32_t k, int32_t B, int tile,
-                                 int32_t* btotals, int (&eb)[KC], int (&dl)[KC]) {
+// Three phases that callers separate with barriers (tile_dedup_ranks below).  After
+// the last: eb[j] is the bucket of the lane's token's j-th entry or kBadBucket, dl[j]
+// the token's rank among the tile's tokens that send to that bucket; btotals[b]
+// (unless null) the tile's distinct-token count of bucket b after the second.
+template <int KC, int NW, int TT>
+__device__ __forceinline__ void dedup_phase_ballots(TileLds<KC, NW, TT>& lds, int32_t M, int32_t k,
+                                                    int32_t B, int tile, int (&eb)[KC]) {
   constexpr int TW = TT / 64;  // token waves
   static_assert(TW <= NW, "every token has a lane");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = wave_index();
   const bool token_wave = w < TW;
-  const uint64_t below = (1ull << lane) - 1ull;
   const int64_t t = (int64_t)tile * TT + (int64_t)w * 64 + lane;
   const bool tv = token_wave && t < M;
   const int* my_ids = lds.ids_s + ((token_wave ? w * 64 : 0) + lane) * k;
@@ -320,19 +336,29 @@ __device__ __forceinline__ void tile_dedup_ranks(TileLds<KC, NW, TT>& lds, int32
     lds.wbal[w][lane] = mine;
     lds.wbcnt[w][lane] = __builtin_popcountll(mine);
   }
-  __syncthreads();
+}
+template <int KC, int NW, int TT>
+__device__ __forceinline__ void dedup_phase_prefix(TileLds<KC, NW, TT>& lds, int32_t B,
+                                                   int32_t* btotals) {
+  const int tid = threadIdx.x;
   if (tid < B) {
     int run = 0;
 #pragma unroll
-    for (int ww = 0; ww < TW; ++ww) {
+    for (int ww = 0; ww < TT / 64; ++ww) {
       const int v = lds.wbcnt[ww][tid];
       lds.wbcnt[ww][tid] = run;
       run += v;
     }
     if (btotals != nullptr) btotals[tid] = run;
   }
-  __syncthreads();
-  const int wt = token_wave ? w : 0;  // waves without tokens read a valid row, unused
+}
+template <int KC, int NW, int TT>
+__device__ __forceinline__ void dedup_phase_finish(TileLds<KC, NW, TT>& lds, const int (&eb)[KC],
+                                                   int (&dl)[KC]) {
+  const int lane = threadIdx.x & 63;
+  const int w = wave_index();
+  const uint64_t below = (1ull << lane) - 1ull;
+  const int wt = w < TT / 64 ? w : 0;  // waves without tokens read a valid row, unused
 #pragma unroll
   for (int j = 0; j < KC; ++j) {
     const int b = eb[j] != kBadBucket ? eb[j] : 0;
@@ -340,6 +366,17 @@ __device__ __forceinline__ void tile_dedup_ranks(TileLds<KC, NW, TT>& lds, int32
     const uint64_t bal = lds.wbal[wt][b];
     dl[j] = eb[j] != kBadBucket ? base + __builtin_popcountll(bal & below) : -1;
   }
+}
+
+template <int KC, int NW = kTileWaves, int TT = kTileTokens>
+__device__ __forceinline__ void tile_dedup_ranks(TileLds<KC, NW, TT>& lds, int32_t M, int32_t k,
+                                                 int32_t B, int tile, int32_t* btotals,
+                                                 int (&eb)[KC], int (&dl)[KC]) {
+  dedup_phase_ballots<KC, NW, TT>(lds, M, k, B, tile, eb);
+  __syncthreads();
+  dedup_phase_prefix<KC, NW, TT>(lds, B, btotals);
+  __syncthreads();
+  dedup_phase_finish<KC, NW, TT>(lds, eb, dl);
 }
 
 // Distinct-token counts of the tile's buckets, token view as in tile_dedup_ranks:
@@ -1209,12 +1246,20 @@ __global__ __launch_bounds__((onepass_waves<KC, TT>() * 64)) void layout_onepass
   }
 
   // While the counts travel (a store and a load across the chip take longer than
-  // the work below): this tile's ranks (the first barrier inside also orders the
-  // publication's reads of pre_s before it is overwritten below) ...
+  // the work below): this tile's ranks (the first barrier also orders the
+  // publication's reads of pre_s before it is overwritten below).  With dedup, the
+  // tokens' bucket ranks run in the same phases, between the same barriers: their few
+  // latency-bound waves use issue slots the matching leaves free ...
   int rc[NC];
-  tile_rank_entries<KC, NC, NW, TT>(lds, G, ok, ec, nullptr, rc);
   int eb[KC], dl[KC];
-  if (dedup) tile_dedup_ranks<KC, NW, TT>(lds, M, k, B, tile, nullptr, eb, dl);
+  rank_phase_match<KC, NC, NW, TT>(lds, G, ok, ec, rc);
+  if (dedup) dedup_phase_ballots<KC, NW, TT>(lds, M, k, B, tile, eb);
+  __syncthreads();
+  rank_phase_prefix<KC, NW, TT>(lds, G, nullptr);
+  if (dedup) dedup_phase_prefix<KC, NW, TT>(lds, B, nullptr);
+  __syncthreads();
+  rank_phase_finish<KC, NC, NW, TT>(lds, ec, rc);
+  if (dedup) dedup_phase_finish<KC, NW, TT>(lds, eb, dl);
   // ... and the experts' (bucket, id) order: id order for a contiguous map, where the
   // buckets (map[e-1], map[e]] start at expert e; else ranked by bucket
   if (sorted_map_s) {
