@@ -1248,8 +1248,8 @@ __global__ __launch_bounds__((onepass_waves<KC, TT>() * 64)) void layout_onepass
   // While the counts travel (a store and a load across the chip take longer than
   // the work below): this tile's ranks (the first barrier also orders the
   // publication's reads of pre_s before it is overwritten below).  With dedup, the
-  // tokens' bucket ranks run in the same phases, between the same barriers: their few
-  // latency-bound waves use issue slots the matching leaves free ...
+  // tokens' bucket ranks run in the same phases, between the same barriers, instead
+  // of after them ...
   int rc[NC];
   int eb[KC], dl[KC];
   rank_phase_match<KC, NC, NW, TT>(lds, G, ok, ec, rc);
