@@ -11,7 +11,8 @@
 //    routing-pattern expert placement ...", the copy-reduction item).
 //
 // Building blocks (device functions shared by the kernels below):
-//  - tile_expert_ranks: one 256-thread workgroup, 256 tokens.  Each wave64 holds NC
+//  - tile_expert_ranks (tile_load_ids, then the rank phases): one workgroup of NW
+//    waves per tile of TT tokens (256 unless stated).  Each wave64 holds NC
 //    consecutive 64-entry chunks of the tile's (t, j) entries in flat order.  Entries
 //    of a chunk that name the same expert are found with ceil(log2 G) ballots (lanes
 //    agreeing on every bit of the id), the ballots of all chunks interleaved; per
@@ -21,12 +22,14 @@
 //    the leader.  No same-address LDS atomics under skew.  That value plus the lane's
 //    rank among its peers (mbcnt) is the entry's stable rank in the wave; a cross-wave
 //    prefix makes it the rank in the tile.
-//  - tile_dedup_ranks: token view (lane = token).  Per-token bucket bitmask; one
-//    ballot per bucket gives each token's rank among the tile's tokens sending there.
-//  - expert_order_offsets: experts ranked by (bucket, id) with the same ballot
-//    matching (key = bucket), then a block-wide exclusive scan of the counts in that
-//    order gives every expert's offset; a map whose bucket never decreases with the
-//    id skips the ranking (id order).
+//  - tile_dedup_ranks (in phases too): token view (lane = token).  Per-token bucket
+//    bitmask; one ballot per bucket gives each token's rank among the tile's tokens
+//    sending there.
+//  - expert_sigma_positions / expert_order_offsets: experts ranked by (bucket, id)
+//    with the same ballot matching (key = bucket), from the map alone; then a
+//    block-wide exclusive scan of the counts in that order gives every expert's
+//    offset; a map whose bucket never decreases with the id skips the ranking (id
+//    order).
 //
 // Kernels:
 //  - M <= 256 tokens (one tile): layout_single_kernel does everything in LDS in one
@@ -34,8 +37,10 @@
 //  - M <= 512 with the row scatter in the same launch: layout_dispatch_small_kernel
 //    (every workgroup recomputes the layout in LDS, then copies its share of rows).
 //  - 2 to kOnePassMaxTiles tiles (M <= 16384): layout_onepass_kernel, one launch.
-//    Each tile publishes its counts, waits (bounded) until every tile has, reduces
-//    the columns it needs itself and writes its slots from registers.  Up to
+//    Each tile counts its entries and publishes the counts, ranks its entries and
+//    orders the experts while the other tiles' counts arrive, waits (bounded) until
+//    every tile has published, reduces the columns it needs itself and writes its
+//    slots from registers.  Up to
 //    kOnePassMaxTiles tiles of 1024 tokens (M <= 65536, k <= 8) take the same kernel
 //    with 16 waves of one 64-token group each.
 //  - more tiles (or k > 8 above 16384 tokens): three launches, no inter-workgroup
