@@ -653,7 +653,15 @@ __global__ __launch_bounds__(kTileThreads) void layout_single_kernel(
 // workgroups share the row copies: work item i = (token, 4 KiB piece of its row) goes to
 // workgroup i mod gridDim.x, which loads the piece once (a batch of items at a time, all
 // loads in flight) and stores it non-temporally to each of the token's distinct send
-// rows inside the buffer.  The LDS row table holds each distinct row once (dedup repeats
+// rows inside the buffer.  Without dedup (and k >= 4) the items are 1 KiB pieces
+// instead, and the workgroup's four waves share the token's k rows (wave w stores rows
+// j = w, w + 4, ...), as the separate dispatch kernel spreads its stores over waves:
+// measured (graph replay, N=7168, top-8, this call + combine of its rows) 9.8 / 12.6 /
+// 18.8 us at M = 64 / 128 / 256 against 11.9 / 16.4 / 21.6 with 4 KiB items, the
+// combine after it reading the rows faster (the call alone: 6.4 / 8.2 / 12.1 against
+// 6.5 / 8.1 / 12.3).  In dedup mode the 4 KiB items stay: the waves would share a
+// token's ~4.6 distinct rows unevenly (14.2 vs 14.1 us at M = 128, 20.3 vs 19.4 at 256),
+// and compacting the distinct rows first did not help (14.5, 20.6).  The LDS row table holds each distinct row once (dedup repeats
 // are marked absent while the layout is built), so the scatter reads a token's k rows
 // together and needs no duplicate search.  Issuing the first batch of row loads before
 // the layout work was measured slower (vector-load counters retire in order, so the
@@ -661,6 +669,8 @@ __global__ __launch_bounds__(kTileThreads) void layout_single_kernel(
 // index 0 even when M = 0.
 constexpr int kFusedPieceVecs = kTileThreads;  // 16-byte vectors per work item
 constexpr int kFusedBatch = 4;                  // work items loaded together
+constexpr int kFusedFlatPieceVecs = 64;         // the same, 1 KiB items (no dedup, k >= 4)
+constexpr int kFusedFlatBatch = 2;
 // Grid cap: two workgroups per CU, which fit at once for every instantiation (41-68 KiB
 // of LDS each).  Every workgroup recomputes the layout before copying, so a grid that
 // does not fit at once pays that again in a second wave, while fewer workgroups give
@@ -669,7 +679,7 @@ constexpr int kFusedBatch = 4;                  // work items loaded together
 // at M=256, 45.8 / 36.9 / 36.2 / 46.1 us at M=512; dedup on alike.
 constexpr int kFusedMaxBlocks = 512;
 
-template <int KC, int NTILE, int NC>
+template <int KC, int NTILE, int NC, bool ITEM1K>
 __global__ __launch_bounds__(kTileThreads) void layout_dispatch_small_kernel(
     const int32_t* __restrict__ idx, int32_t M, int32_t k,
     const int32_t* __restrict__ ebkt, int32_t G, int32_t B, int32_t dedup,
@@ -807,6 +817,39 @@ __global__ __launch_bounds__(kTileThreads) void layout_dispatch_small_kernel(
   __syncthreads();
 
   // row scatter
+  if constexpr (ITEM1K) {  // 1 KiB items, the waves share the token's rows (no dedup)
+    constexpr int NWV = kTileThreads / 64;
+    for (int64_t base = blockIdx.x; base < items; base += stride * kFusedFlatBatch) {
+      u32x4 u[kFusedFlatBatch];
+#pragma unroll
+      for (int q = 0; q < kFusedFlatBatch; ++q) {  // clamped, unconditional: all in flight
+        const int64_t it = base + q * stride;
+        const int64_t t = it < items ? it / pieces : 0;
+        const int c = (int)(it - t * pieces) * kFusedFlatPieceVecs + lane;
+        const bool in_row = it < items && c < row_vecs;
+        u[q] = x[in_row ? t * row_vecs + c : 0];
+      }
+#pragma unroll
+      for (int q = 0; q < kFusedFlatBatch; ++q) {
+        const int64_t it = base + q * stride;
+        if (it >= items) break;  // uniform
+        const int t = (int)(it / pieces);
+        const int piece = (int)(it - (int64_t)t * pieces);
+        const int c = piece * kFusedFlatPieceVecs + lane;
+        const int32_t* rows = row_s + t * k;
+        for (int j = w; j < k; j += NWV) {
+          const int r = rows[j];
+          if (r < 0 || r >= out_rows) continue;  // uniform
+          if (c < row_vecs) __builtin_nontemporal_store(u[q], out + (int64_t)r * row_vecs + c);
+          if (x_scale != nullptr && piece == 0) {
+            for (int sc = lane; sc < scale_cols; sc += 64)
+              out_scale[(int64_t)r * scale_cols + sc] = x_scale[(int64_t)t * scale_cols + sc];
+          }
+        }
+      }
+    }
+    return;
+  }
   for (int64_t base = blockIdx.x; base < items; base += stride * kFusedBatch) {
     load_batch(base);  // x may be null only when M = 0, and then there is no item
 #pragma unroll
@@ -1498,16 +1541,29 @@ hipError_t launch_fused(const int32_t* topk_idx, int64_t M, int32_t k, const int
                         int32_t scale_cols, void* out, float* out_scale, int64_t out_rows,
                         hipStream_t stream) {
   const int32_t row_vecs = (int32_t)(row_bytes / 16);
-  const int32_t pieces = (row_vecs + kFusedPieceVecs - 1) / kFusedPieceVecs;
+  const bool item1k = dedup == 0 && k >= 4;
+  const int32_t piece_vecs = item1k ? kFusedFlatPieceVecs : kFusedPieceVecs;
+  const int32_t pieces = (row_vecs + piece_vecs - 1) / piece_vecs;
   const int64_t items = M * pieces;
   const unsigned grid = (unsigned)(items < 1 ? 1 : (items < kFusedMaxBlocks ? items : kFusedMaxBlocks));
   const int32_t* idx = M > 0 ? topk_idx : expert_bucket;  // read at index 0 only
-#define MOEDL_FUSED(NT, NC)                                                                     \
-  hipLaunchKernelGGL((layout_dispatch_small_kernel<KC, NT, NC>), dim3(grid), dim3(kTileThreads), 0, \
-                     stream, idx, (int32_t)M, k, expert_bucket, G, B, dedup, expert_count,         \
-                     expert_offset, bucket_count, bucket_offset, slot, send_row, send_token,      \
-                     status, (const u32x4*)x, row_vecs, pieces, x_scale, scale_cols, (u32x4*)out, \
-                     out_scale, out_rows)
+#define MOEDL_FUSED_AS(NT, NC, ITEM1K)                                                          \
+  hipLaunchKernelGGL((layout_dispatch_small_kernel<KC, NT, NC, ITEM1K>), dim3(grid),               \
+                     dim3(kTileThreads), 0, stream, idx, (int32_t)M, k, expert_bucket, G, B, dedup, \
+                     expert_count, expert_offset, bucket_count, bucket_offset, slot, send_row,     \
+                     send_token, status, (const u32x4*)x, row_vecs, pieces, x_scale, scale_cols,   \
+                     (u32x4*)out, out_scale, out_rows)
+  // (k >= 4 implies KC >= 4: the 1 KiB item shape is compiled only there)
+#define MOEDL_FUSED(NT, NC)                                     \
+  do {                                                          \
+    if constexpr (KC >= 4) {                                    \
+      if (item1k) {                                             \
+        MOEDL_FUSED_AS(NT, NC, true);                           \
+        break;                                                  \
+      }                                                         \
+    }                                                           \
+    MOEDL_FUSED_AS(NT, NC, false);                              \
+  } while (0)
   if (M > kTileTokens) {
     MOEDL_FUSED(2, KC);
   } else {
@@ -1519,6 +1575,7 @@ hipError_t launch_fused(const int32_t* topk_idx, int64_t M, int32_t k, const int
     else MOEDL_FUSED(1, KC >= 16 ? 16 : 1);
   }
 #undef MOEDL_FUSED
+#undef MOEDL_FUSED_AS
   return hipGetLastError();
 }
 
