@@ -51,6 +51,8 @@ KERNEL_SOURCES = {
     "expand": "combine_dispatch_layout_amd/csrc/bucket.hip",
     "combine_partial": "combine_dispatch_layout_amd/csrc/bucket.hip",
     "combine_reduce": "combine_dispatch_layout_amd/csrc/bucket.hip",
+    "layout": "combine_dispatch_layout_amd/csrc/layout.hip",
+    "layout_dispatch": "combine_dispatch_layout_amd/csrc/layout.hip",
 }
 
 
@@ -844,7 +846,15 @@ def bench_small(args, dev):
     best = min(("three_calls", "fused"), key=lambda p: head[f"flat_{p}_graph_us"])
     members = ["layout", "dispatch", "combine"] if best == "three_calls" else ["layout_dispatch", "combine"]
     dom = max(members, key=lambda n: kern_us[n])
-    roofline = hbm_roofline(dom, kern_bytes[dom], kern_us[dom], M=head["M"],
+    # a 2 GiB plain copy: calibrates the HBM byte counters of a profiled run of this leg
+    from combine_dispatch_layout_amd import harness
+    src = torch.empty(1 << 30, dtype=torch.int16, device=dev)
+    dst = torch.empty_like(src)
+    harness.copy(src, dst)
+    torch.cuda.synchronize()
+    del src, dst
+    traffic = recorded_traffic(dom, f"uniform-top8-M{head['M']}-small-path")
+    roofline = hbm_roofline(dom, kern_bytes[dom], kern_us[dom], traffic=traffic, M=head["M"],
                             graph_us_per_kernel={n: round(v, 2) for n, v in kern_us.items()})
     cpu = None if args.no_cpu else cpu_small_baseline(workloads.make_workload(1, M=ms[0]))
     out = {"metric": "small-M layout+dispatch+combine latency (graph replay, us per step)",
