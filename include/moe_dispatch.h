@@ -204,7 +204,9 @@ moe_status moe_dispatch(const void* x, moe_dtype dtype, int64_t M, int32_t N,
  * status word of moe_dispatch_layout (same arguments, same meaning) and the send rows
  * of moe_dispatch (x, dtype, N, x_scale, out, out_scale, out_rows as there).  No
  * workspace is needed.  Within the launch every workgroup derives the layout in its
- * own on-chip memory, so no workgroup waits for another.
+ * own on-chip memory, so no workgroup waits for another.  On MI355X it is the faster
+ * form up to 256 tokens (one tile); from 257 to 512 tokens the two calls are faster,
+ * since every workgroup then derives two tiles.
  * Errors: those of the two calls, and MOE_ERR_UNSUPPORTED for M > MOE_FUSED_MAX_TOKENS.
  */
 #define MOE_FUSED_MAX_TOKENS 512
