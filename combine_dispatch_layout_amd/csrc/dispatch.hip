@@ -137,20 +137,22 @@ hipError_t launch_dispatch(const void* x, int64_t M, int64_t row_bytes, const fl
   const int32_t pieces = (row_vecs + kPieceVecs - 1) / kPieceVecs;
   const int64_t blocks = M * pieces;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  // The k single-store waves shape is the faster one while x's reads are served by the
-  // 256 MB Infinity Cache: 6.1-6.7 TB/s against 5.8 for two waves at x = 235 MB.  Once
-  // they reach HBM it falls to ~3.5-3.8 TB/s, while the shape of two waves sharing a
-  // token's rows (about four stores per load) holds 4.8-5.5: at a fixed 1.88 GB send
-  // buffer, x = 470 MB (k = 4) runs at 4.1 vs 5.3 TB/s, x = 940 MB (k = 2) at 5.0 vs
-  // 5.6; at k = 1 the shapes are within 4% (5.65 vs 5.44).  The send-buffer size itself
-  // does not matter (1.88 GB written inside a 4 GiB allocation, or a 2.35 GB buffer
-  // with x below the cache, behave like their x).  Nor does the latency the storing
-  // waves see: with x prefetched into L2 ahead of them (their loads return in ~275
-  // instead of ~1,600 cycles) the k-wave shape is no faster.  Measured on MI355X with
-  // rocprofv3 read-latency counters; the threshold sits between x = 235 MB (k-wave
-  // faster) and 264 MB (two-wave faster).  An x that fits can still have been pushed out
-  // of the cache by the kernels before the dispatch; the caller who knows that can ask
-  // for the two-wave shape with the dedup flag, which selects the shape only.
+  // The k single-store waves shape is the faster one while x fits the 256 MB Infinity
+  // Cache: 6.1-6.7 TB/s against 5.8 for two waves at x = 235 MB.  Once x outgrows it,
+  // the dispatch's own plain x loads leave lines in the caches, and with such lines
+  // present (left by any earlier kernel's plain loads or stores too) the k-wave shape
+  // falls to ~3.5-3.8 TB/s, while the shape of two waves sharing a token's rows (about
+  // four stores per load) holds 4.8-5.5: at a fixed 1.88 GB send buffer, x = 470 MB
+  // (k = 4) runs at 4.1 vs 5.3 TB/s, x = 940 MB (k = 2) at 5.0 vs 5.6; at k = 1 the
+  // shapes are within 4% (5.65 vs 5.44).  The send-buffer size itself does not matter
+  // (1.88 GB written inside a 4 GiB allocation, or a 2.35 GB buffer with x below the
+  // cache, behave like their x).  Nor does the latency the storing waves see: with x
+  // prefetched into L2 ahead of them (their loads return in ~275 instead of ~1,600
+  // cycles) the k-wave shape is no faster.  Measured on MI355X with rocprofv3
+  // read-latency counters; the threshold sits between x = 235 MB (k-wave faster) and
+  // 264 MB (two-wave faster).  A caller whose earlier kernels leave plainly accessed
+  // lines behind can ask for the two-wave shape with the dedup flag, which selects the
+  // shape only.
   constexpr int64_t kCacheResidentXBytes = (int64_t)240 << 20;
   if (dedup || (k >= 2 && M * row_bytes > kCacheResidentXBytes)) {
 #define MOEDL_CASE(K)                                                                          \
