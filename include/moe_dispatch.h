@@ -150,7 +150,10 @@ moe_status moe_dispatch_layout(const int32_t* topk_idx, int64_t M, int32_t k,
  * about 850,000 tokens).  The call runs on the current device (`stream` must belong
  * to it).  Every call on one GPU shares that GPU's array: calls that overlap in time
  * race, calls ordered on a stream do not.  Nothing is allocated and no memset is
- * issued; the array starts zero-filled and every call leaves it in that state.
+ * issued: the array starts zero-filled, the state a new workspace must be in, and
+ * every call leaves it ready for the next one, as moe_dispatch_layout does with
+ * its workspace (the header and the region the next call publishes in are
+ * cleared by the kernels).
  */
 #define MOE_LAYOUT_SCRATCH_BYTES (4u << 20)
 
