@@ -366,6 +366,24 @@ def bench_placement(args, w, dev):
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
+def _time_calls(torch, calls, steps):
+    """Mean event time (us) of each call over `steps` rounds, after one warm-up round."""
+    for c in calls:
+        c()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+          for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(stream)
+        for c, e in zip(calls, ev[i][1:]):
+            c()
+            e.record(stream)
+    torch.cuda.synchronize()
+    return [float(np.mean([e[q].elapsed_time(e[q + 1]) for e in ev])) * 1e3
+            for q in range(len(calls))]
+
+
 def _time_gemm(moedl, torch, x, wt, tiles, y, lay_offset, lay_count, steps, warmup):
     """Mean event time (us) of moe_grouped_gemm_tiles and moe_grouped_gemm over `steps`."""
     rows = x.shape[0]
@@ -390,7 +408,9 @@ def bench_gemm(args, w, dev):
     """The expert step over the headline layout: every dispatched row (M*k of them,
     slot-indexed by expert) times its expert's [Nout, N] bf16 weights, fp32 accumulate.
     Also the grouped-GEMM shape the DeepSpeed page measures (16 experts, 760 tokens,
-    dim 2048 -> hidden 768, unbalanced), as context."""
+    dim 2048 -> hidden 768, unbalanced), as context, and the regular form of the
+    headline problem (M*k/G rows per expert) run by the vendor's batched product and by
+    this library, interleaved, as the reference for the grouped kernel."""
     import torch
     from combine_dispatch_layout_amd import moedl
     M, N, G, k, B = w.M, w.N, w.G, w.k, w.B
@@ -437,6 +457,29 @@ def bench_gemm(args, w, dev):
     ys = torch.empty((Ms, Ns), dtype=torch.int16, device=dev)
     s_tiles, s_gemm = _time_gemm(moedl, torch, xs, ws, ts, ys, offd, cntd, args.steps, args.warmup)
 
+    # The vendor library on the regular form of the same problem: every expert given
+    # M*k/G rows, so that hipBLASLt's batched product (torch.bmm, per-expert weights,
+    # contiguous operands) can run it; this library's grouped GEMM on the same regular
+    # layout beside it, interleaved.  The batched product has no ragged rows to handle,
+    # so it is the reference for the grouped kernel's own bodies.
+    E = (M * k) // G
+    xb = xe[:G * E].view(torch.bfloat16).view(G, E, N)
+    w_kn = wt.view(torch.bfloat16).transpose(1, 2).contiguous()
+    yb = torch.empty((G, E, Nout), dtype=torch.bfloat16, device=dev)
+    offr = torch.arange(0, G, device=dev, dtype=torch.int32) * E
+    cntr = torch.full((G,), E, dtype=torch.int32, device=dev)
+    tr = moedl.moe_grouped_gemm_tiles(offr, cntr, G * E)
+    yr = torch.empty((G * E, Nout), dtype=torch.int16, device=dev)
+    flops_r = 2.0 * G * E * N * Nout
+    vend, lib_r = [], []
+    for _ in range(3):
+        vend.append(flops_r / (_time_calls(torch, [lambda: torch.bmm(xb, w_kn, out=yb)], 5)[0]
+                               * 1e-6) / 1e12)
+        lib_r.append(flops_r / (_time_gemm(moedl, torch, xe[:G * E], wt, tr, yr, offr, cntr, 5,
+                                           1)[1] * 1e-6) / 1e12)
+    del w_kn, yb, yr
+    torch.cuda.synchronize()
+
     # a 2 GiB plain copy: calibrates the HBM byte counters of a profiled run of this leg
     from combine_dispatch_layout_amd import harness
     src = torch.empty(1 << 30, dtype=torch.int16, device=dev)
@@ -464,6 +507,11 @@ def bench_gemm(args, w, dev):
                                                         + M * k * Nout * 2)},
            "cpu_baseline": cpu,
            "event_us": {"grouped_gemm_tiles": round(t_tiles, 2), "grouped_gemm": round(t_gemm, 2)},
+           "regular_layout_reference": {
+               "experts": G, "rows_per_expert": E, "K": N, "Nout": Nout,
+               "vendor_batched_tflops": [round(v, 1) for v in vend],
+               "grouped_gemm_tflops": [round(v, 1) for v in lib_r],
+               "vendor": "torch.bmm (hipBLASLt), per-expert weights, contiguous operands"},
            "deepspeed_page_shape": {"experts": Gs, "tokens": Ms, "K": Ks, "Nout": Ns,
                                     "tiles_us": round(s_tiles, 2), "gemm_us": round(s_gemm, 2),
                                     "tflops": round(2.0 * Ms * Ks * Ns / (s_gemm * 1e-6) / 1e12, 2)}}
@@ -573,6 +621,29 @@ def bench_chain(args, w, dev):
     traffic = recorded_traffic("grouped_gemm", wl_name,
                                os.path.join(PROFILES, f"hbm_traffic_{wl_name}.txt"))
 
+    # The vendor library on the regular form of the same problem: every expert given
+    # M*k/G rows, so that hipBLASLt's batched product (torch.bmm, per-expert weights,
+    # contiguous operands) can run it; this library's grouped GEMM on the same regular
+    # layout beside it, interleaved.  The batched product has no ragged rows to handle,
+    # so it is the reference for the grouped kernel's own bodies.
+    E = (M * k) // G
+    xb = xe[:G * E].view(torch.bfloat16).view(G, E, N)
+    w_kn = wt.view(torch.bfloat16).transpose(1, 2).contiguous()
+    yb = torch.empty((G, E, Nout), dtype=torch.bfloat16, device=dev)
+    offr = torch.arange(0, G, device=dev, dtype=torch.int32) * E
+    cntr = torch.full((G,), E, dtype=torch.int32, device=dev)
+    tr = moedl.moe_grouped_gemm_tiles(offr, cntr, G * E)
+    yr = torch.empty((G * E, Nout), dtype=torch.int16, device=dev)
+    flops_r = 2.0 * G * E * N * Nout
+    vend, lib_r = [], []
+    for _ in range(3):
+        vend.append(flops_r / (_time_calls(torch, [lambda: torch.bmm(xb, w_kn, out=yb)], 5)[0]
+                               * 1e-6) / 1e12)
+        lib_r.append(flops_r / (_time_gemm(moedl, torch, xe[:G * E], wt, tr, yr, offr, cntr, 5,
+                                           1)[1] * 1e-6) / 1e12)
+    del w_kn, yb, yr
+    torch.cuda.synchronize()
+
     # a 2 GiB plain copy: calibrates the HBM byte counters of a profiled run of this leg
     from combine_dispatch_layout_amd import harness
     src = torch.empty(1 << 30, dtype=torch.int16, device=dev)
@@ -653,6 +724,29 @@ def bench_dispatch_x(args, dev):
             row[f"{n}_gbps"] = round(alg / us / 1e3, 1)
         rows.append(row)
         del out, x, y, lay, idx
+
+    # The vendor library on the regular form of the same problem: every expert given
+    # M*k/G rows, so that hipBLASLt's batched product (torch.bmm, per-expert weights,
+    # contiguous operands) can run it; this library's grouped GEMM on the same regular
+    # layout beside it, interleaved.  The batched product has no ragged rows to handle,
+    # so it is the reference for the grouped kernel's own bodies.
+    E = (M * k) // G
+    xb = xe[:G * E].view(torch.bfloat16).view(G, E, N)
+    w_kn = wt.view(torch.bfloat16).transpose(1, 2).contiguous()
+    yb = torch.empty((G, E, Nout), dtype=torch.bfloat16, device=dev)
+    offr = torch.arange(0, G, device=dev, dtype=torch.int32) * E
+    cntr = torch.full((G,), E, dtype=torch.int32, device=dev)
+    tr = moedl.moe_grouped_gemm_tiles(offr, cntr, G * E)
+    yr = torch.empty((G * E, Nout), dtype=torch.int16, device=dev)
+    flops_r = 2.0 * G * E * N * Nout
+    vend, lib_r = [], []
+    for _ in range(3):
+        vend.append(flops_r / (_time_calls(torch, [lambda: torch.bmm(xb, w_kn, out=yb)], 5)[0]
+                               * 1e-6) / 1e12)
+        lib_r.append(flops_r / (_time_gemm(moedl, torch, xe[:G * E], wt, tr, yr, offr, cntr, 5,
+                                           1)[1] * 1e-6) / 1e12)
+    del w_kn, yb, yr
+    torch.cuda.synchronize()
 
     # a 2 GiB plain copy: calibrates the HBM byte counters of a profiled run of this leg
     from combine_dispatch_layout_amd import harness
@@ -846,6 +940,29 @@ def bench_small(args, dev):
     best = min(("three_calls", "fused"), key=lambda p: head[f"flat_{p}_graph_us"])
     members = ["layout", "dispatch", "combine"] if best == "three_calls" else ["layout_dispatch", "combine"]
     dom = max(members, key=lambda n: kern_us[n])
+    # The vendor library on the regular form of the same problem: every expert given
+    # M*k/G rows, so that hipBLASLt's batched product (torch.bmm, per-expert weights,
+    # contiguous operands) can run it; this library's grouped GEMM on the same regular
+    # layout beside it, interleaved.  The batched product has no ragged rows to handle,
+    # so it is the reference for the grouped kernel's own bodies.
+    E = (M * k) // G
+    xb = xe[:G * E].view(torch.bfloat16).view(G, E, N)
+    w_kn = wt.view(torch.bfloat16).transpose(1, 2).contiguous()
+    yb = torch.empty((G, E, Nout), dtype=torch.bfloat16, device=dev)
+    offr = torch.arange(0, G, device=dev, dtype=torch.int32) * E
+    cntr = torch.full((G,), E, dtype=torch.int32, device=dev)
+    tr = moedl.moe_grouped_gemm_tiles(offr, cntr, G * E)
+    yr = torch.empty((G * E, Nout), dtype=torch.int16, device=dev)
+    flops_r = 2.0 * G * E * N * Nout
+    vend, lib_r = [], []
+    for _ in range(3):
+        vend.append(flops_r / (_time_calls(torch, [lambda: torch.bmm(xb, w_kn, out=yb)], 5)[0]
+                               * 1e-6) / 1e12)
+        lib_r.append(flops_r / (_time_gemm(moedl, torch, xe[:G * E], wt, tr, yr, offr, cntr, 5,
+                                           1)[1] * 1e-6) / 1e12)
+    del w_kn, yb, yr
+    torch.cuda.synchronize()
+
     # a 2 GiB plain copy: calibrates the HBM byte counters of a profiled run of this leg
     from combine_dispatch_layout_amd import harness
     src = torch.empty(1 << 30, dtype=torch.int16, device=dev)
