@@ -117,3 +117,38 @@ def test_fused_bad_ids_and_map(gpu_lib, dedup):
     lay, _, _ = fused(w, dedup)
     torch.cuda.synchronize()
     assert int(lay.status.item()) == -8
+
+
+def _random_fused_cases(n=20, seed=20261204):
+    """Seeded random shapes within the one-launch path (M <= 512): one tile and two,
+    both row dtypes (fp8 with scales when N is a multiple of 128), repeats, every
+    bucket map, both modes."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        G = int(rng.choice([1, 2, 7, 32, 64, 256, 1000, 1024]))
+        k = int(rng.integers(1, min(16, G) + 1))
+        B = int(rng.integers(1, 65))
+        M = int(rng.integers(1, moedl.FUSED_MAX_TOKENS + 1))
+        dtype = "fp8" if rng.random() < 0.3 else "bf16"
+        if dtype == "fp8":
+            N = int(rng.integers(1, 17)) * 128 if rng.random() < 0.6 else int(rng.integers(1, 128)) * 16
+        else:
+            N = int(rng.integers(1, 1025)) * 8
+        routing = "repeats" if rng.random() < 0.3 else "uniform"
+        bmap = str(rng.choice(["contiguous", "random", "roundrobin"]))
+        dedup = bool(rng.random() < 0.5)
+        cases.append((M, N, G, k, B, dtype, routing, bmap, dedup))
+    return cases
+
+
+RANDOM_FUSED = _random_fused_cases()
+
+
+@pytest.mark.parametrize("case", RANDOM_FUSED, ids=[
+    f"M{c[0]}-N{c[1]}-G{c[2]}-k{c[3]}-B{c[4]}-{c[5]}-{c[6]}-{c[7]}-{'dedup' if c[8] else 'flat'}"
+    for c in RANDOM_FUSED])
+def test_fused_random_shapes(gpu_lib, case):
+    M, N, G, k, B, dtype, routing, bmap, dedup = case
+    w = wl.make_custom(M, N, G, k, B, dtype=dtype, routing=routing, bucket_map=bmap, seed=M + N)
+    check(w, dedup, f"fused {w.name} map={bmap} scales={w.x_scale is not None} dedup={dedup}")
