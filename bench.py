@@ -621,29 +621,6 @@ def bench_chain(args, w, dev):
     traffic = recorded_traffic("grouped_gemm", wl_name,
                                os.path.join(PROFILES, f"hbm_traffic_{wl_name}.txt"))
 
-    # The vendor library on the regular form of the same problem: every expert given
-    # M*k/G rows, so that hipBLASLt's batched product (torch.bmm, per-expert weights,
-    # contiguous operands) can run it; this library's grouped GEMM on the same regular
-    # layout beside it, interleaved.  The batched product has no ragged rows to handle,
-    # so it is the reference for the grouped kernel's own bodies.
-    E = (M * k) // G
-    xb = xe[:G * E].view(torch.bfloat16).view(G, E, N)
-    w_kn = wt.view(torch.bfloat16).transpose(1, 2).contiguous()
-    yb = torch.empty((G, E, Nout), dtype=torch.bfloat16, device=dev)
-    offr = torch.arange(0, G, device=dev, dtype=torch.int32) * E
-    cntr = torch.full((G,), E, dtype=torch.int32, device=dev)
-    tr = moedl.moe_grouped_gemm_tiles(offr, cntr, G * E)
-    yr = torch.empty((G * E, Nout), dtype=torch.int16, device=dev)
-    flops_r = 2.0 * G * E * N * Nout
-    vend, lib_r = [], []
-    for _ in range(3):
-        vend.append(flops_r / (_time_calls(torch, [lambda: torch.bmm(xb, w_kn, out=yb)], 5)[0]
-                               * 1e-6) / 1e12)
-        lib_r.append(flops_r / (_time_gemm(moedl, torch, xe[:G * E], wt, tr, yr, offr, cntr, 5,
-                                           1)[1] * 1e-6) / 1e12)
-    del w_kn, yb, yr
-    torch.cuda.synchronize()
-
     # a 2 GiB plain copy: calibrates the HBM byte counters of a profiled run of this leg
     from combine_dispatch_layout_amd import harness
     src = torch.empty(1 << 30, dtype=torch.int16, device=dev)
@@ -724,29 +701,6 @@ def bench_dispatch_x(args, dev):
             row[f"{n}_gbps"] = round(alg / us / 1e3, 1)
         rows.append(row)
         del out, x, y, lay, idx
-
-    # The vendor library on the regular form of the same problem: every expert given
-    # M*k/G rows, so that hipBLASLt's batched product (torch.bmm, per-expert weights,
-    # contiguous operands) can run it; this library's grouped GEMM on the same regular
-    # layout beside it, interleaved.  The batched product has no ragged rows to handle,
-    # so it is the reference for the grouped kernel's own bodies.
-    E = (M * k) // G
-    xb = xe[:G * E].view(torch.bfloat16).view(G, E, N)
-    w_kn = wt.view(torch.bfloat16).transpose(1, 2).contiguous()
-    yb = torch.empty((G, E, Nout), dtype=torch.bfloat16, device=dev)
-    offr = torch.arange(0, G, device=dev, dtype=torch.int32) * E
-    cntr = torch.full((G,), E, dtype=torch.int32, device=dev)
-    tr = moedl.moe_grouped_gemm_tiles(offr, cntr, G * E)
-    yr = torch.empty((G * E, Nout), dtype=torch.int16, device=dev)
-    flops_r = 2.0 * G * E * N * Nout
-    vend, lib_r = [], []
-    for _ in range(3):
-        vend.append(flops_r / (_time_calls(torch, [lambda: torch.bmm(xb, w_kn, out=yb)], 5)[0]
-                               * 1e-6) / 1e12)
-        lib_r.append(flops_r / (_time_gemm(moedl, torch, xe[:G * E], wt, tr, yr, offr, cntr, 5,
-                                           1)[1] * 1e-6) / 1e12)
-    del w_kn, yb, yr
-    torch.cuda.synchronize()
 
     # a 2 GiB plain copy: calibrates the HBM byte counters of a profiled run of this leg
     from combine_dispatch_layout_amd import harness
@@ -940,29 +894,6 @@ def bench_small(args, dev):
     best = min(("three_calls", "fused"), key=lambda p: head[f"flat_{p}_graph_us"])
     members = ["layout", "dispatch", "combine"] if best == "three_calls" else ["layout_dispatch", "combine"]
     dom = max(members, key=lambda n: kern_us[n])
-    # The vendor library on the regular form of the same problem: every expert given
-    # M*k/G rows, so that hipBLASLt's batched product (torch.bmm, per-expert weights,
-    # contiguous operands) can run it; this library's grouped GEMM on the same regular
-    # layout beside it, interleaved.  The batched product has no ragged rows to handle,
-    # so it is the reference for the grouped kernel's own bodies.
-    E = (M * k) // G
-    xb = xe[:G * E].view(torch.bfloat16).view(G, E, N)
-    w_kn = wt.view(torch.bfloat16).transpose(1, 2).contiguous()
-    yb = torch.empty((G, E, Nout), dtype=torch.bfloat16, device=dev)
-    offr = torch.arange(0, G, device=dev, dtype=torch.int32) * E
-    cntr = torch.full((G,), E, dtype=torch.int32, device=dev)
-    tr = moedl.moe_grouped_gemm_tiles(offr, cntr, G * E)
-    yr = torch.empty((G * E, Nout), dtype=torch.int16, device=dev)
-    flops_r = 2.0 * G * E * N * Nout
-    vend, lib_r = [], []
-    for _ in range(3):
-        vend.append(flops_r / (_time_calls(torch, [lambda: torch.bmm(xb, w_kn, out=yb)], 5)[0]
-                               * 1e-6) / 1e12)
-        lib_r.append(flops_r / (_time_gemm(moedl, torch, xe[:G * E], wt, tr, yr, offr, cntr, 5,
-                                           1)[1] * 1e-6) / 1e12)
-    del w_kn, yb, yr
-    torch.cuda.synchronize()
-
     # a 2 GiB plain copy: calibrates the HBM byte counters of a profiled run of this leg
     from combine_dispatch_layout_amd import harness
     src = torch.empty(1 << 30, dtype=torch.int16, device=dev)
