@@ -856,8 +856,27 @@ def bench_small(args, dev):
                 moedl.moe_layout_dispatch(idx, ebkt, B, dedup, x, lay=lay, out=out)
                 moedl.moe_combine(eo, wts, lay.slot, y=y)
 
+            # the same two forms as prepared calls (arguments checked and marshalled
+            # once): eager steps without the binding's per-call checks
+            p_lay, _ = moedl.prepare_dispatch_layout(idx, ebkt, B, dedup, out=lay)
+            p_disp, _, _ = moedl.prepare_dispatch(x, lay.send_row, cap, out=out, dedup=dedup)
+            p_comb, _ = moedl.prepare_combine(eo, wts, lay.slot, y=y)
+            p_fused, _, _, _ = moedl.prepare_layout_dispatch(idx, ebkt, B, dedup, x, lay=lay,
+                                                             out=out)
+
+            def three_prepared():
+                p_lay()
+                p_disp()
+                p_comb()
+
+            def fused_prepared():
+                p_fused()
+                p_comb()
+
             tag = "dedup" if dedup else "flat"
-            for name, fn in (("three_calls", three), ("fused", fused)):
+            for name, fn in (("three_calls", three), ("fused", fused),
+                             ("three_calls_prepared", three_prepared),
+                             ("fused_prepared", fused_prepared)):
                 for _ in range(max(1, args.warmup)):
                     fn()
                 torch.cuda.synchronize()

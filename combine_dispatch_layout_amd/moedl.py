@@ -200,9 +200,14 @@ def alloc_layout(M: int, k: int, G: int, B: int, dedup: bool, device="cuda") -> 
         dedup=dedup)
 
 
-def moe_dispatch_layout(topk_idx: torch.Tensor, expert_bucket: torch.Tensor, B: int,
-                        dedup: bool, out: Optional[Layout] = None, stream=None) -> Layout:
-    """topk_idx int32 [M, k], expert_bucket int32 [G] -> Layout (device tensors)."""
+def _layout_tensors(lay: "Layout") -> tuple:
+    return (lay.expert_count, lay.expert_offset, lay.bucket_count, lay.bucket_offset, lay.slot,
+            lay.send_row, lay.send_token, lay.status, lay.workspace)
+
+
+def _dispatch_layout_args(topk_idx, expert_bucket, B, dedup, out):
+    """Checked arguments of moe_dispatch_layout (all but the stream), the tensors they
+    point into, and the Layout."""
     M, k = topk_idx.shape
     G = expert_bucket.shape[0]
     if topk_idx.dtype != torch.int32 or expert_bucket.dtype != torch.int32:
@@ -212,12 +217,18 @@ def moe_dispatch_layout(topk_idx: torch.Tensor, expert_bucket: torch.Tensor, B: 
     else:
         lay = out
         _check_layout(lay, M, k, G, B, dedup)
-    st = lib().moe_dispatch_layout(
-        _ptr(topk_idx), M, k, _ptr(expert_bucket), G, B, int(dedup), _ptr(lay.expert_count),
-        _ptr(lay.expert_offset), _ptr(lay.bucket_count), _ptr(lay.bucket_offset),
-        _ptr(lay.slot), _ptr(lay.send_row), _ptr(lay.send_token), _ptr(lay.status),
-        _ptr(lay.workspace), lay.workspace.numel(), _stream(stream, topk_idx))
-    _check("moe_dispatch_layout", st)
+    args = (_ptr(topk_idx), M, k, _ptr(expert_bucket), G, B, int(dedup), _ptr(lay.expert_count),
+            _ptr(lay.expert_offset), _ptr(lay.bucket_count), _ptr(lay.bucket_offset),
+            _ptr(lay.slot), _ptr(lay.send_row), _ptr(lay.send_token), _ptr(lay.status),
+            _ptr(lay.workspace), lay.workspace.numel())
+    return args, (topk_idx, expert_bucket) + _layout_tensors(lay), lay
+
+
+def moe_dispatch_layout(topk_idx: torch.Tensor, expert_bucket: torch.Tensor, B: int,
+                        dedup: bool, out: Optional[Layout] = None, stream=None) -> Layout:
+    """topk_idx int32 [M, k], expert_bucket int32 [G] -> Layout (device tensors)."""
+    args, _, lay = _dispatch_layout_args(topk_idx, expert_bucket, B, dedup, out)
+    _check("moe_dispatch_layout", lib().moe_dispatch_layout(*args, _stream(stream, topk_idx)))
     return lay
 
 
@@ -262,12 +273,7 @@ def _dtype_code(x: torch.Tensor) -> int:
     raise TypeError(f"unsupported row dtype {x.dtype}")
 
 
-def moe_dispatch(x: torch.Tensor, send_row: torch.Tensor, out_rows: int,
-                 x_scale: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-                 out_scale: Optional[torch.Tensor] = None, dedup: bool = False, stream=None):
-    """x [M, N] (bf16 bits or fp8 codes), send_row int32 [M, k] -> (out [out_rows, N],
-    out_scale [out_rows, N/128] or None).  dedup: send_row came from a dedup layout
-    (selects the kernel shape only)."""
+def _dispatch_args(x, send_row, out_rows, x_scale, out, out_scale, dedup):
     M, N = x.shape
     k = send_row.shape[1] if send_row.dim() == 2 else 1
     if out is None:
@@ -280,21 +286,27 @@ def moe_dispatch(x: torch.Tensor, send_row: torch.Tensor, out_rows: int,
     _want(out, "out", _row_dtypes(x), out_rows * N, cols=N)
     _want(x_scale, "x_scale", _F32, M * sc)
     _want(out_scale, "out_scale", _F32, out_rows * sc)
-    st = lib().moe_dispatch(_ptr(x), _dtype_code(x), M, N, _ptr(x_scale), _ptr(send_row), k,
-                            int(dedup), _ptr(out), _ptr(out_scale), out_rows, _stream(stream, x))
-    _check("moe_dispatch", st)
+    args = (_ptr(x), _dtype_code(x), M, N, _ptr(x_scale), _ptr(send_row), k, int(dedup),
+            _ptr(out), _ptr(out_scale), out_rows)
+    return args, (x, send_row, x_scale, out, out_scale), out, out_scale
+
+
+def moe_dispatch(x: torch.Tensor, send_row: torch.Tensor, out_rows: int,
+                 x_scale: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                 out_scale: Optional[torch.Tensor] = None, dedup: bool = False, stream=None):
+    """x [M, N] (bf16 bits or fp8 codes), send_row int32 [M, k] -> (out [out_rows, N],
+    out_scale [out_rows, N/128] or None).  dedup: send_row came from a dedup layout
+    (selects the kernel shape only)."""
+    args, _, out, out_scale = _dispatch_args(x, send_row, out_rows, x_scale, out, out_scale,
+                                             dedup)
+    _check("moe_dispatch", lib().moe_dispatch(*args, _stream(stream, x)))
     return out, out_scale
 
 
 FUSED_MAX_TOKENS = 512
 
 
-def moe_layout_dispatch(topk_idx: torch.Tensor, expert_bucket: torch.Tensor, B: int,
-                        dedup: bool, x: torch.Tensor, x_scale: Optional[torch.Tensor] = None,
-                        lay: Optional[Layout] = None, out: Optional[torch.Tensor] = None,
-                        out_scale: Optional[torch.Tensor] = None, stream=None):
-    """moe_dispatch_layout + moe_dispatch in one launch (M <= 512) -> (Layout, out,
-    out_scale).  The Layout's workspace is not used."""
+def _layout_dispatch_args(topk_idx, expert_bucket, B, dedup, x, x_scale, lay, out, out_scale):
     M, k = topk_idx.shape
     G = expert_bucket.shape[0]
     N = x.shape[1]
@@ -315,18 +327,27 @@ def moe_layout_dispatch(topk_idx: torch.Tensor, expert_bucket: torch.Tensor, B: 
     _want(out, "out", _row_dtypes(x), 0, cols=N)
     _want(x_scale, "x_scale", _F32, M * sc)
     _want(out_scale, "out_scale", _F32, out.shape[0] * sc)
-    st = lib().moe_layout_dispatch(
-        _ptr(topk_idx), M, k, _ptr(expert_bucket), G, B, int(dedup), _ptr(x), _dtype_code(x), N,
-        _ptr(x_scale), _ptr(lay.expert_count), _ptr(lay.expert_offset), _ptr(lay.bucket_count),
-        _ptr(lay.bucket_offset), _ptr(lay.slot), _ptr(lay.send_row), _ptr(lay.send_token),
-        _ptr(lay.status), _ptr(out), _ptr(out_scale), out.shape[0], _stream(stream, topk_idx))
-    _check("moe_layout_dispatch", st)
+    args = (_ptr(topk_idx), M, k, _ptr(expert_bucket), G, B, int(dedup), _ptr(x), _dtype_code(x),
+            N, _ptr(x_scale), _ptr(lay.expert_count), _ptr(lay.expert_offset),
+            _ptr(lay.bucket_count), _ptr(lay.bucket_offset), _ptr(lay.slot), _ptr(lay.send_row),
+            _ptr(lay.send_token), _ptr(lay.status), _ptr(out), _ptr(out_scale), out.shape[0])
+    keep = (topk_idx, expert_bucket, x, x_scale, out, out_scale) + _layout_tensors(lay)
+    return args, keep, lay, out, out_scale
+
+
+def moe_layout_dispatch(topk_idx: torch.Tensor, expert_bucket: torch.Tensor, B: int,
+                        dedup: bool, x: torch.Tensor, x_scale: Optional[torch.Tensor] = None,
+                        lay: Optional[Layout] = None, out: Optional[torch.Tensor] = None,
+                        out_scale: Optional[torch.Tensor] = None, stream=None):
+    """moe_dispatch_layout + moe_dispatch in one launch (M <= 512) -> (Layout, out,
+    out_scale).  The Layout's workspace is not used."""
+    args, _, lay, out, out_scale = _layout_dispatch_args(topk_idx, expert_bucket, B, dedup, x,
+                                                         x_scale, lay, out, out_scale)
+    _check("moe_layout_dispatch", lib().moe_layout_dispatch(*args, _stream(stream, topk_idx)))
     return lay, out, out_scale
 
 
-def moe_combine(expert_out: torch.Tensor, weights: torch.Tensor, slot: torch.Tensor,
-                y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """expert_out bf16 [rows, N], weights fp32 [M, k], slot int32 [M, k] -> y bf16 [M, N]."""
+def _combine_args(expert_out, weights, slot, y):
     rows, N = expert_out.shape
     M, k = slot.shape
     _want(expert_out, "expert_out", _ROW16, 0)
@@ -335,10 +356,81 @@ def moe_combine(expert_out: torch.Tensor, weights: torch.Tensor, slot: torch.Ten
     if y is None:
         y = torch.empty((M, N), dtype=expert_out.dtype, device=expert_out.device)
     _want(y, "y", _ROW16, M * N, cols=N)
-    st = lib().moe_combine(_ptr(expert_out), rows, _ptr(weights), _ptr(slot), M, k, N, _ptr(y),
-                           _stream(stream, slot))
-    _check("moe_combine", st)
+    args = (_ptr(expert_out), rows, _ptr(weights), _ptr(slot), M, k, N, _ptr(y))
+    return args, (expert_out, weights, slot, y), y
+
+
+def moe_combine(expert_out: torch.Tensor, weights: torch.Tensor, slot: torch.Tensor,
+                y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """expert_out bf16 [rows, N], weights fp32 [M, k], slot int32 [M, k] -> y bf16 [M, N]."""
+    args, _, y = _combine_args(expert_out, weights, slot, y)
+    _check("moe_combine", lib().moe_combine(*args, _stream(stream, slot)))
     return y
+
+
+class Prepared:
+    """One library call whose arguments were checked and marshalled once, for loops
+    that repeat a call on the same buffers (a serving step at small M spends more
+    time in the binding than on the GPU).  It holds references to every tensor it was
+    built from, so their storage, and the device pointers taken from it, stay valid
+    while it lives.  Calling it launches on the stream given when it was prepared,
+    else on the current stream of the tensors' device, and raises MoeError on an error
+    status.  The tensors' contents may change between calls; for other tensors or
+    sizes, prepare a new call."""
+
+    __slots__ = ("_name", "_fn", "_args", "_dev", "_stream", "_keep")
+
+    def __init__(self, name: str, args: tuple, like: torch.Tensor, keep: tuple, stream):
+        self._name = name
+        self._fn = getattr(lib(), name)
+        self._args = args
+        self._dev = like.get_device()
+        self._stream = None if stream is None else _stream(stream)
+        self._keep = keep
+
+    def __call__(self) -> None:
+        s = self._stream
+        if s is None:
+            s = (_raw_stream(self._dev) if _raw_stream is not None
+                 else torch.cuda.current_stream(self._dev).cuda_stream)
+        st = self._fn(*self._args, s)
+        if st != MOE_OK:
+            raise MoeError(self._name, st)
+
+
+def prepare_dispatch_layout(topk_idx: torch.Tensor, expert_bucket: torch.Tensor, B: int,
+                            dedup: bool, out: Optional[Layout] = None, stream=None):
+    """moe_dispatch_layout as a Prepared call -> (Prepared, Layout).  Nothing is
+    launched until the Prepared is called."""
+    args, keep, lay = _dispatch_layout_args(topk_idx, expert_bucket, B, dedup, out)
+    return Prepared("moe_dispatch_layout", args, topk_idx, keep, stream), lay
+
+
+def prepare_dispatch(x: torch.Tensor, send_row: torch.Tensor, out_rows: int,
+                     x_scale: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                     out_scale: Optional[torch.Tensor] = None, dedup: bool = False,
+                     stream=None):
+    """moe_dispatch as a Prepared call -> (Prepared, out, out_scale)."""
+    args, keep, out, out_scale = _dispatch_args(x, send_row, out_rows, x_scale, out, out_scale,
+                                                dedup)
+    return Prepared("moe_dispatch", args, x, keep, stream), out, out_scale
+
+
+def prepare_layout_dispatch(topk_idx: torch.Tensor, expert_bucket: torch.Tensor, B: int,
+                            dedup: bool, x: torch.Tensor, x_scale: Optional[torch.Tensor] = None,
+                            lay: Optional[Layout] = None, out: Optional[torch.Tensor] = None,
+                            out_scale: Optional[torch.Tensor] = None, stream=None):
+    """moe_layout_dispatch as a Prepared call -> (Prepared, Layout, out, out_scale)."""
+    args, keep, lay, out, out_scale = _layout_dispatch_args(topk_idx, expert_bucket, B, dedup, x,
+                                                            x_scale, lay, out, out_scale)
+    return Prepared("moe_layout_dispatch", args, topk_idx, keep, stream), lay, out, out_scale
+
+
+def prepare_combine(expert_out: torch.Tensor, weights: torch.Tensor, slot: torch.Tensor,
+                    y: Optional[torch.Tensor] = None, stream=None):
+    """moe_combine as a Prepared call -> (Prepared, y)."""
+    args, keep, y = _combine_args(expert_out, weights, slot, y)
+    return Prepared("moe_combine", args, slot, keep, stream), y
 
 
 def moe_expand(recv: torch.Tensor, send_row: torch.Tensor, slot: torch.Tensor, expert_rows: int,

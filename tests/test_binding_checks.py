@@ -122,3 +122,27 @@ def test_right_sizes_reach_the_device_check(built_lib):
     _raises(ValueError, "must live on the GPU", moedl.moe_combine,
             torch.zeros((M * k, N), dtype=torch.int16), torch.zeros((M, k)),
             torch.zeros((M, k), **i32))
+
+
+def test_prepared_calls_check_like_the_calls(built_lib):
+    """prepare_* run the checks of the immediate calls when they are built, and the
+    device check after them; nothing is launched while preparing."""
+    M, k, G, B, N = 10, 4, 16, 2, 256
+    idx = torch.zeros((M, k), **i32)
+    ebkt = torch.zeros(G, **i32)
+    lay = moedl.alloc_layout(M, k, G, B, False, device="cpu")
+    lay.slot = torch.empty(M * k - 1, **i32)
+    _raises(ValueError, "slot: 39 elements, the call needs 40", moedl.prepare_dispatch_layout,
+            idx, ebkt, B, False, out=lay)
+    _raises(ValueError, "must live on the GPU", moedl.prepare_dispatch_layout, idx, ebkt, B,
+            False, out=moedl.alloc_layout(M, k, G, B, False, device="cpu"))
+    x = torch.zeros((M, N), dtype=torch.int16)
+    _raises(ValueError, "out: 256 elements", moedl.prepare_dispatch, x,
+            torch.zeros((M, k), **i32), M * k, out=torch.zeros((1, N), dtype=torch.int16))
+    _raises(ValueError, "x: 256 elements, the call needs 2560", moedl.prepare_layout_dispatch,
+            idx, ebkt, B, False, x[:1])
+    eo = torch.zeros((M * k, N), dtype=torch.int16)
+    _raises(ValueError, "weights: 16 elements", moedl.prepare_combine, eo,
+            torch.zeros((4, k)), torch.zeros((M, k), **i32))
+    _raises(ValueError, "must live on the GPU", moedl.prepare_combine, eo,
+            torch.zeros((M, k)), torch.zeros((M, k), **i32))

@@ -152,3 +152,48 @@ def test_fused_random_shapes(gpu_lib, case):
     M, N, G, k, B, dtype, routing, bmap, dedup = case
     w = wl.make_custom(M, N, G, k, B, dtype=dtype, routing=routing, bucket_map=bmap, seed=M + N)
     check(w, dedup, f"fused {w.name} map={bmap} scales={w.x_scale is not None} dedup={dedup}")
+
+
+@pytest.mark.parametrize("dedup", [False, True])
+def test_prepared_calls_match_immediate_calls(gpu_lib, dedup):
+    """Prepared calls (arguments checked and marshalled once) give the immediate calls'
+    bytes, follow in-place changes of their inputs' contents, and run on the stream they
+    were prepared with."""
+    say(f"prepared calls dedup={dedup}")
+    w1 = wl.make_workload(1)                                        # M = 64
+    w2 = wl.make_custom(w1.M, w1.N, w1.G, w1.k, w1.B, seed=7)      # same shapes, new contents
+    idx, ebkt = dev(w1.topk_idx).clone(), dev(w1.expert_bucket)
+    x = rows_dev(w1).clone()
+    wts = dev(w1.weights).clone()
+    side = torch.cuda.Stream()
+    p_lay, lay = moedl.prepare_dispatch_layout(idx, ebkt, w1.B, dedup)
+    p_disp, out, _ = moedl.prepare_dispatch(x, lay.send_row, lay.capacity, dedup=dedup)
+    p_fused, flay, fout, _ = moedl.prepare_layout_dispatch(idx, ebkt, w1.B, dedup, x,
+                                                           stream=side)
+    p_comb, y = moedl.prepare_combine(out, wts, lay.slot) if not dedup else (None, None)
+    for w in (w1, w2, w1):
+        idx.copy_(dev(w.topk_idx))
+        x.copy_(rows_dev(w))
+        wts.copy_(dev(w.weights))
+        p_lay()
+        p_disp()
+        if p_comb is not None:
+            p_comb()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            p_fused()
+        torch.cuda.current_stream().wait_stream(side)
+        ref_lay = moedl.moe_dispatch_layout(idx, ebkt, w.B, dedup)
+        ref_out, _ = moedl.moe_dispatch(x, ref_lay.send_row, ref_lay.capacity, dedup=dedup)
+        torch.cuda.synchronize()
+        R = int(ref_lay.bucket_offset[w.B].item())
+        for got in (lay, flay):
+            for name in ("expert_count", "expert_offset", "bucket_count", "bucket_offset",
+                         "slot", "send_row", "status"):
+                assert torch.equal(getattr(got, name), getattr(ref_lay, name)), name
+            assert torch.equal(got.send_token[:R], ref_lay.send_token[:R])
+        assert torch.equal(out[:R], ref_out[:R]) and torch.equal(fout[:R], ref_out[:R])
+        if p_comb is not None:
+            ref_y = moedl.moe_combine(ref_out, wts, ref_lay.slot)
+            torch.cuda.synchronize()
+            assert torch.equal(y, ref_y)
