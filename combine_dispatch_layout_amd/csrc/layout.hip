@@ -42,8 +42,8 @@
 //    every tile has published, reduces the columns it needs itself and writes its
 //    slots from registers.  Up to
 //    kOnePassMaxTiles tiles of 1024 tokens (M <= 65536, k <= 8) take the same kernel
-//    with 16 waves of one 64-token group each; at k >= 5, while 3 to kOnePassMaxTiles
-//    tiles of 128 tokens cover M (M <= 8192), it takes those instead.
+//    with 16 waves of one 64-token group each; at k >= 5 it takes tiles of 64 tokens
+//    (8 waves) for 257 <= M <= 2048 and of 128 tokens for M <= 8192 instead.
 //  - more tiles (or k > 8 above 16384 tokens): three launches, no inter-workgroup
 //    waiting:
 //    layout_tile_kernel (per-tile ranks and totals to the workspace),
@@ -1100,6 +1100,7 @@ __global__ __launch_bounds__(256) void layout_finalize_kernel(
 constexpr int kSpinLimit = 1 << 20;  // polls (about 1 us each) before giving up
 constexpr int kWideTileTokens = 1024;  // tokens per tile above kOnePassMaxTiles 256-token tiles
 constexpr int kSmallTileTokens = 128;  // tokens per tile where 128-token tiles fit one launch
+constexpr int kTinyTileTokens = 64;    // tokens per tile where up to 32 such tiles cover M
 constexpr int kRawBufferWord3 = 0x00020000;  // raw buffer resource: no format, no swizzle
 constexpr int kSc1 = 16;  // cache policy sc1: coherent across the XCDs' L2s
 
@@ -1188,10 +1189,13 @@ __device__ __forceinline__ bool poll_column_sums(const int32_t* rows, int T, int
 
 // Waves of the one-launch layout's workgroup.  Tiles of 256 tokens: 16 (two 64-entry
 // chunks per wave at k = 8) when k > 2, else 4 * KC so that every wave holds at least
-// one chunk; tiles of 128 tokens (KC >= 8 only): 16, one chunk per wave at k = 8.  Tiles of 1024 tokens (more than 64 tiles of 256): 16, one per 64 tokens,
+// one chunk; tiles of 128 tokens (KC >= 8 only): 16, one chunk per wave at k = 8; tiles
+// of 64 tokens (KC >= 8 only): 8, one chunk per wave at k = 8.  Tiles of 1024 tokens (more than 64 tiles of 256): 16, one per 64 tokens,
 // KC chunks each.
 template <int KC, int TT = kTileTokens>
-constexpr int onepass_waves() { return TT > kTileTokens ? TT / 64 : (KC >= 4 ? 16 : 4 * KC); }
+constexpr int onepass_waves() {
+  return TT > kTileTokens ? TT / 64 : TT == 64 ? 8 : (KC >= 4 ? 16 : 4 * KC);
+}
 
 template <int KC, int TT>
 __global__ __launch_bounds__((onepass_waves<KC, TT>() * 64)) void layout_onepass_kernel(
@@ -1496,12 +1500,22 @@ void launch_tiles(const int32_t* topk_idx, int64_t M, int32_t k, const int32_t* 
 #undef MOEDL_SINGLE
     return;
   }
-  // 128-token tiles while 3 to kOnePassMaxTiles of them cover M (k >= 5, so that each of
-  // the 16 waves still holds one 64-entry chunk): half the ranking work per workgroup
-  // for twice the published rows read.  Measured on MI355X (graph replay, outputs
-  // identical): M = 1,000 8.5 -> 7.5 us, 4,096 9.0 -> 8.2 (Zipf 8.8 -> 8.0), 8,192
-  // 9.3 -> 8.7; dedup layouts 0.6-0.9 us faster as well.
+  // Smaller tiles where at most kOnePassMaxTiles of them cover M (k >= 5, so that every
+  // wave still holds one 64-entry chunk): less ranking work per workgroup for more
+  // published rows read.  Measured on MI355X (graph replay, outputs identical), 256 /
+  // 128 / 64-token tiles: M = 1,000 8.5 / 7.6 / 7.1 us, 2,048 8.6 / 7.8 / 7.4, 4,096 9.0 /
+  // 8.1 / 8.8 (64 rows read: the 64-token tiles lose there), 8,192 9.3 / 8.6; dedup
+  // layouts likewise.  So 64-token tiles up to 32 of them, 128-token tiles up to 64.
   if constexpr (KC >= 8) {
+    const int64_t T64 = (M + kTinyTileTokens - 1) / kTinyTileTokens;
+    if (T64 >= 2 && T64 <= kOnePassMaxTiles / 2) {
+      hipLaunchKernelGGL((layout_onepass_kernel<KC, kTinyTileTokens>), dim3((unsigned)T64),
+                         dim3(onepass_waves<KC, kTinyTileTokens>() * 64), 0, stream, topk_idx,
+                         (int32_t)M, k, expert_bucket, G, B, dedup, expert_count, expert_offset,
+                         bucket_count, bucket_offset, slot, send_row, send_token, status,
+                         ws.header, ws.region[0], ws.region[1]);
+      return;
+    }
     const int64_t T128 = (M + kSmallTileTokens - 1) / kSmallTileTokens;
     if (T128 >= 3 && T128 <= kOnePassMaxTiles) {
       hipLaunchKernelGGL((layout_onepass_kernel<KC, kSmallTileTokens>), dim3((unsigned)T128),

@@ -176,8 +176,10 @@ EDGE = [  # (M, N, G, k, B, dtype, routing, bucket_map)
     (333, 16, 64, 8, 8, "fp8", "uniform", "contiguous"),         # fp8, no scales
     (200, 8192, 128, 2, 2, "bf16", "uniform", "contiguous"),     # 16 KiB rows
     (90, 12288, 64, 3, 4, "bf16", "uniform", "contiguous"),      # rows above 16 KiB
-    (257, 64, 32, 5, 4, "bf16", "repeats", "random"),            # 3 tiles of 128 tokens (k >= 5)
-    (384, 96, 1024, 16, 64, "bf16", "uniform", "random"),        # 3 tiles of 128 at max G, k, B
+    (257, 64, 32, 5, 4, "bf16", "repeats", "random"),            # 5 tiles of 64 tokens (k >= 5)
+    (384, 96, 1024, 16, 64, "bf16", "uniform", "random"),        # 6 tiles of 64 at max G, k, B
+    (2048, 64, 256, 8, 8, "bf16", "uniform", "random"),          # 32 tiles of 64 tokens
+    (2049, 64, 256, 8, 8, "bf16", "uniform", "random"),          # 17 tiles of 128 tokens
     (8192, 64, 256, 8, 8, "bf16", "uniform", "roundrobin"),      # 64 tiles of 128 tokens
     (8193, 64, 256, 8, 8, "bf16", "uniform", "roundrobin"),      # 33 tiles of 256 tokens
     (8192, 64, 64, 4, 8, "bf16", "uniform", "random"),           # k = 4: 32 tiles of 256
