@@ -42,8 +42,9 @@
 //    every tile has published, reduces the columns it needs itself and writes its
 //    slots from registers.  Up to
 //    kOnePassMaxTiles tiles of 1024 tokens (M <= 65536, k <= 8) take the same kernel
-//    with 16 waves of one 64-token group each; at k >= 5 it takes tiles of 64 tokens
-//    (8 waves) for 257 <= M <= 2048 and of 128 tokens for M <= 8192 instead.
+//    with 16 waves of one 64-token group each (tiles of 512 tokens, 8 such waves, for
+//    M <= 32768); at k >= 5 it takes tiles of 64 tokens (8 waves) for 257 <= M <= 2048
+//    and of 128 tokens for M <= 8192 instead.
 //  - more tiles (or k > 8 above 16384 tokens): three launches, no inter-workgroup
 //    waiting:
 //    layout_tile_kernel (per-tile ranks and totals to the workspace),
@@ -1101,6 +1102,7 @@ constexpr int kSpinLimit = 1 << 20;  // polls (about 1 us each) before giving up
 constexpr int kWideTileTokens = 1024;  // tokens per tile above kOnePassMaxTiles 256-token tiles
 constexpr int kSmallTileTokens = 128;  // tokens per tile where 128-token tiles fit one launch
 constexpr int kTinyTileTokens = 64;    // tokens per tile where up to 32 such tiles cover M
+constexpr int kHalfWideTileTokens = 512;  // tokens per tile where 64 such tiles cover M
 constexpr int kRawBufferWord3 = 0x00020000;  // raw buffer resource: no format, no swizzle
 constexpr int kSc1 = 16;  // cache policy sc1: coherent across the XCDs' L2s
 
@@ -1534,10 +1536,22 @@ void launch_tiles(const int32_t* topk_idx, int64_t M, int32_t k, const int32_t* 
                        ws.header, ws.region[0], ws.region[1]);
     return;
   }
-  // up to 64 tiles of 1024 tokens (M <= 65,536), k <= 8: the same single launch with
-  // four times the tokens per workgroup (k = 16 would not fit its ids in LDS)
+  // up to 64 tiles of 512 tokens (M <= 32,768), else of 1024 tokens (M <= 65,536), k <= 8:
+  // the same single launch with more tokens per workgroup (k = 16 would not fit the
+  // ids of a 1024-token tile in LDS).  Measured on MI355X (graph replay, outputs
+  // identical), 1024- against 512-token tiles: M = 16,385 15.9 -> 11.9 us, 20,000 16.1
+  // -> 12.5, 32,768 16.4 -> 13.9 (Zipf 15.5 -> 13.6); dedup layouts 3-5 us faster.
   const int64_t T4 = (M + kWideTileTokens - 1) / kWideTileTokens;
   if constexpr (KC <= 8) {
+    const int64_t T2 = (M + kHalfWideTileTokens - 1) / kHalfWideTileTokens;
+    if (T2 >= 2 && T2 <= kOnePassMaxTiles) {
+      hipLaunchKernelGGL((layout_onepass_kernel<KC, kHalfWideTileTokens>), dim3((unsigned)T2),
+                         dim3(onepass_waves<KC, kHalfWideTileTokens>() * 64), 0, stream,
+                         topk_idx, (int32_t)M, k, expert_bucket, G, B, dedup, expert_count,
+                         expert_offset, bucket_count, bucket_offset, slot, send_row,
+                         send_token, status, ws.header, ws.region[0], ws.region[1]);
+      return;
+    }
     if (T4 >= 2 && T4 <= kOnePassMaxTiles) {
       hipLaunchKernelGGL((layout_onepass_kernel<KC, kWideTileTokens>), dim3((unsigned)T4),
                          dim3(onepass_waves<KC, kWideTileTokens>() * 64), 0, stream, topk_idx,

@@ -184,7 +184,9 @@ EDGE = [  # (M, N, G, k, B, dtype, routing, bucket_map)
     (8193, 64, 256, 8, 8, "bf16", "uniform", "roundrobin"),      # 33 tiles of 256 tokens
     (8192, 64, 64, 4, 8, "bf16", "uniform", "random"),           # k = 4: 32 tiles of 256
     (16384, 64, 1024, 16, 64, "bf16", "uniform", "random"),      # 64 tiles, one launch, max G, k, B
-    (16385, 64, 256, 8, 8, "bf16", "uniform", "random"),         # one launch, 1024-token tiles
+    (16385, 64, 256, 8, 8, "bf16", "uniform", "random"),         # one launch, 33 tiles of 512
+    (32768, 32, 256, 8, 8, "bf16", "repeats", "random"),         # 64 tiles of 512 tokens
+    (32769, 32, 256, 8, 8, "bf16", "uniform", "roundrobin"),     # 33 tiles of 1024 tokens
     (16385, 64, 256, 9, 8, "bf16", "uniform", "random"),         # k = 9 there: three launches
     (65537, 16, 64, 2, 4, "bf16", "uniform", "random"),          # 65 tiles of 1024: three launches
 ]
