@@ -235,11 +235,7 @@ def moe_dispatch_layout(topk_idx: torch.Tensor, expert_bucket: torch.Tensor, B: 
 LAYOUT_SCRATCH_BYTES = 4 << 20  # the library's static workspace per GPU
 
 
-def moe_dispatch_layout_noalloc(topk_idx: torch.Tensor, expert_bucket: torch.Tensor, B: int,
-                                dedup: bool, out: Optional[Layout] = None,
-                                stream=None) -> Layout:
-    """moe_dispatch_layout with the library's static workspace (no workspace buffer).
-    The Layout's workspace field is an empty tensor."""
+def _dispatch_layout_noalloc_args(topk_idx, expert_bucket, B, dedup, out):
     M, k = topk_idx.shape
     G = expert_bucket.shape[0]
     if topk_idx.dtype != torch.int32 or expert_bucket.dtype != torch.int32:
@@ -256,12 +252,20 @@ def moe_dispatch_layout_noalloc(topk_idx: torch.Tensor, expert_bucket: torch.Ten
     else:
         lay = out
         _check_layout(lay, M, k, G, B, dedup)
-    st = lib().moe_dispatch_layout_noalloc(
-        _ptr(topk_idx), M, k, _ptr(expert_bucket), G, B, int(dedup), _ptr(lay.expert_count),
-        _ptr(lay.expert_offset), _ptr(lay.bucket_count), _ptr(lay.bucket_offset),
-        _ptr(lay.slot), _ptr(lay.send_row), _ptr(lay.send_token), _ptr(lay.status),
-        _stream(stream, topk_idx))
-    _check("moe_dispatch_layout_noalloc", st)
+    args = (_ptr(topk_idx), M, k, _ptr(expert_bucket), G, B, int(dedup), _ptr(lay.expert_count),
+            _ptr(lay.expert_offset), _ptr(lay.bucket_count), _ptr(lay.bucket_offset),
+            _ptr(lay.slot), _ptr(lay.send_row), _ptr(lay.send_token), _ptr(lay.status))
+    return args, (topk_idx, expert_bucket) + _layout_tensors(lay), lay
+
+
+def moe_dispatch_layout_noalloc(topk_idx: torch.Tensor, expert_bucket: torch.Tensor, B: int,
+                                dedup: bool, out: Optional[Layout] = None,
+                                stream=None) -> Layout:
+    """moe_dispatch_layout with the library's static workspace (no workspace buffer).
+    The Layout's workspace field is an empty tensor."""
+    args, _, lay = _dispatch_layout_noalloc_args(topk_idx, expert_bucket, B, dedup, out)
+    _check("moe_dispatch_layout_noalloc",
+           lib().moe_dispatch_layout_noalloc(*args, _stream(stream, topk_idx)))
     return lay
 
 
@@ -404,6 +408,15 @@ def prepare_dispatch_layout(topk_idx: torch.Tensor, expert_bucket: torch.Tensor,
     launched until the Prepared is called."""
     args, keep, lay = _dispatch_layout_args(topk_idx, expert_bucket, B, dedup, out)
     return Prepared("moe_dispatch_layout", args, topk_idx, keep, stream), lay
+
+
+def prepare_dispatch_layout_noalloc(topk_idx: torch.Tensor, expert_bucket: torch.Tensor,
+                                    B: int, dedup: bool, out: Optional[Layout] = None,
+                                    stream=None):
+    """moe_dispatch_layout_noalloc as a Prepared call -> (Prepared, Layout): nothing is
+    allocated when it is called."""
+    args, keep, lay = _dispatch_layout_noalloc_args(topk_idx, expert_bucket, B, dedup, out)
+    return Prepared("moe_dispatch_layout_noalloc", args, topk_idx, keep, stream), lay
 
 
 def prepare_dispatch(x: torch.Tensor, send_row: torch.Tensor, out_rows: int,

@@ -136,6 +136,8 @@ def test_prepared_calls_check_like_the_calls(built_lib):
             idx, ebkt, B, False, out=lay)
     _raises(ValueError, "must live on the GPU", moedl.prepare_dispatch_layout, idx, ebkt, B,
             False, out=moedl.alloc_layout(M, k, G, B, False, device="cpu"))
+    _raises(ValueError, "slot: 39 elements", moedl.prepare_dispatch_layout_noalloc, idx, ebkt,
+            B, False, out=lay)
     x = torch.zeros((M, N), dtype=torch.int16)
     _raises(ValueError, "out: 256 elements", moedl.prepare_dispatch, x,
             torch.zeros((M, k), **i32), M * k, out=torch.zeros((1, N), dtype=torch.int16))

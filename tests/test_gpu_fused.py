@@ -171,11 +171,13 @@ def test_prepared_calls_match_immediate_calls(gpu_lib, dedup):
     p_fused, flay, fout, _ = moedl.prepare_layout_dispatch(idx, ebkt, w1.B, dedup, x,
                                                            stream=side)
     p_comb, y = moedl.prepare_combine(out, wts, lay.slot) if not dedup else (None, None)
+    p_na, nlay = moedl.prepare_dispatch_layout_noalloc(idx, ebkt, w1.B, dedup)
     for w in (w1, w2, w1):
         idx.copy_(dev(w.topk_idx))
         x.copy_(rows_dev(w))
         wts.copy_(dev(w.weights))
         p_lay()
+        p_na()
         p_disp()
         if p_comb is not None:
             p_comb()
@@ -187,7 +189,7 @@ def test_prepared_calls_match_immediate_calls(gpu_lib, dedup):
         ref_out, _ = moedl.moe_dispatch(x, ref_lay.send_row, ref_lay.capacity, dedup=dedup)
         torch.cuda.synchronize()
         R = int(ref_lay.bucket_offset[w.B].item())
-        for got in (lay, flay):
+        for got in (lay, flay, nlay):
             for name in ("expert_count", "expert_offset", "bucket_count", "bucket_offset",
                          "slot", "send_row", "status"):
                 assert torch.equal(getattr(got, name), getattr(ref_lay, name)), name
